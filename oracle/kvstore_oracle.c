@@ -1,0 +1,256 @@
+/*
+ * CPU oracle for the KV-cache store.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path loads this file or
+ * the library built from it: only the tests, the package smoke check and the
+ * benchmark's CPU-baseline leg do.  It shares no code, header, table or helper
+ * with the HIP library; the two meet only in the seeded inputs they are fed.
+ *
+ * Plain, slow, single-threaded C.  Build: gcc -O2 -ffp-contract=off -shared
+ * -fPIC kvstore_oracle.c -lm.  No vectorisation tricks, no blocking, no
+ * fusion: one token at a time, one element at a time, in the order the pages
+ * describe.
+ *
+ * What it follows:
+ *   - Scatter copy: sglang "kvcache.cuh", section store_kvcache / copy_kv_warp:
+ *     token t's K and V rows are copied byte for byte to cache row indices[t];
+ *     the index must satisfy 0 <= index < size_limit (the page asserts it on
+ *     the device).  Here a bad index is counted and its row skipped.
+ *   - Fused FP8 paged store: sglang "trtllm_fp8_kv_kernel.py", kernel
+ *     _fused_fp8_set_kv_buffer_kernel and helper _process_kv_tensor:
+ *     page = loc / page_size, offset = loc % page_size; each element is
+ *     loaded, multiplied in fp32 by the tensor's inverse scale (1.0 when no
+ *     scale is given) and cast to float8 e4m3; the byte lands at
+ *     page*s_page + offset*s_offset + head*s_head + dim.
+ *   - The e4m3fn encoding is written from the format definition named on that
+ *     page (torch.float8_e4m3fn): 1 sign bit, 4 exponent bits with bias 7,
+ *     3 mantissa bits, no infinities, NaN = S.1111.111, largest finite 448.
+ *     The cast's rounding and overflow are not stated on the pages; the reading
+ *     taken is round-to-nearest-even with saturation to +-448 (a NaN stays a
+ *     NaN and keeps its sign).
+ *
+ * Parity pins (all in tests/, CPU only): exhaustive nearest-value search over
+ * the decoded e4m3fn table for every bf16 and fp16 pattern, torch's own
+ * float8_e4m3fn cast where it does not overflow, hand-derived closed-form
+ * values, and store invariants (sentinel, round trip, paged == flat, OOB
+ * skip, permutation invariance, brute force on tiny inputs).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------------- */
+/* Input element decoding.                                                  */
+/* ---------------------------------------------------------------------- */
+
+/* bfloat16 is the upper 16 bits of an IEEE binary32. */
+static float bf16_to_float(uint16_t b) {
+    uint32_t w = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &w, sizeof f);
+    return f;
+}
+
+/* IEEE binary16: 1 sign, 5 exponent bits (bias 15), 10 fraction bits. */
+static float fp16_to_float(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double mag;
+    if (e == 0) {
+        mag = ldexp((double)m, -24);             /* subnormal: m * 2^-24 */
+    } else if (e == 31) {
+        if (m != 0) {
+            /* NaN: keep the sign, keep it quiet */
+            uint32_t w = ((uint32_t)sign << 31) | 0x7FC00000u | ((uint32_t)m << 13);
+            float f;
+            memcpy(&f, &w, sizeof f);
+            return f;
+        }
+        mag = INFINITY;
+    } else {
+        mag = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    }
+    return (float)(sign ? -mag : mag);           /* exact: fits in binary32 */
+}
+
+static float src_to_float(uint16_t bits, int src_is_fp16) {
+    return src_is_fp16 ? fp16_to_float(bits) : bf16_to_float(bits);
+}
+
+/* ---------------------------------------------------------------------- */
+/* fp32 multiply by the inverse scale.                                      */
+/* ---------------------------------------------------------------------- */
+
+/*
+ * y = x * inv rounded once to binary32.  Both operands are binary32, so their
+ * exact product has at most 48 significant bits and is exact in binary64;
+ * converting it to float is then the single round-to-nearest of an fp32
+ * multiply, independent of FMA contraction or x87 excess precision.
+ * A NaN operand propagates itself (keeping its sign); a NaN made from two
+ * non-NaN operands (inf * 0) is the positive default NaN.
+ */
+static float mul_f32(float x, float inv) {
+    if (isnan(x)) return x;
+    if (isnan(inv)) return inv;
+    double p = (double)x * (double)inv;
+    if (isnan(p)) return NAN;
+    return (float)p;
+}
+
+/* ---------------------------------------------------------------------- */
+/* float -> e4m3fn, round to nearest even, saturate to +-448.               */
+/* ---------------------------------------------------------------------- */
+
+/* Round-half-to-even of a non-negative double whose fractional part is exact. */
+static double round_half_even(double q) {
+    double fl = floor(q);
+    double frac = q - fl;
+    if (frac > 0.5) return fl + 1.0;
+    if (frac < 0.5) return fl;
+    return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+}
+
+uint8_t oracle_e4m3fn_from_float(float y) {
+    uint8_t s = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y)) return (uint8_t)(0x7F | s);
+    double a = fabs((double)y);
+    if (a > 448.0) return (uint8_t)(0x7E | s);   /* includes +-inf */
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: value = m * 2^-9, m in 0..7; m == 8 is the
+           smallest normal 2^-6, whose code 0x08 continues the sequence. */
+        double m = round_half_even(a * 512.0);   /* exact scaling by 2^9 */
+        return (uint8_t)((uint8_t)m | s);
+    }
+    int ex;
+    frexp(a, &ex);                               /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1;                              /* floor(log2 a), >= -6 */
+    double m = round_half_even(ldexp(a, 3 - e)); /* a / 2^(e-3), in [8, 16] */
+    if (m == 16.0) {                             /* rounding carried into the exponent */
+        e += 1;
+        m = 8.0;
+    }
+    return (uint8_t)((((e + 7) << 3) | ((int)m - 8)) | s);
+}
+
+/* One element of the fused store: decode, scale, encode. */
+static uint8_t quantize_one(uint16_t bits, int src_is_fp16, float inv) {
+    float x = src_to_float(bits, src_is_fp16);
+    return oracle_e4m3fn_from_float(mul_f32(x, inv));
+}
+
+/* ---------------------------------------------------------------------- */
+/* Exported element helpers (for pins).                                    */
+/* ---------------------------------------------------------------------- */
+
+float oracle_src_to_float(uint16_t bits, int src_is_fp16) {
+    return src_to_float(bits, src_is_fp16);
+}
+
+float oracle_mul_f32(float x, float inv) { return mul_f32(x, inv); }
+
+/* out[i] = e4m3fn(src[i] * inv); inv == NULL means 1.0. */
+void oracle_quantize(const uint16_t* src, int64_t n, int src_is_fp16, const float* inv,
+                     uint8_t* out) {
+    float s = inv ? *inv : 1.0f;
+    for (int64_t i = 0; i < n; ++i) out[i] = quantize_one(src[i], src_is_fp16, s);
+}
+
+void oracle_e4m3fn_array(const float* y, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3fn_from_float(y[i]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* Stores.                                                                  */
+/* ---------------------------------------------------------------------- */
+
+static int64_t read_index(const void* indices, int idx_is_i64, int64_t pos) {
+    if (idx_is_i64) return ((const int64_t*)indices)[pos];
+    return (int64_t)((const int32_t*)indices)[pos];
+}
+
+/* Records a rejected token: count it, keep the smallest token id. */
+static void note_bad(int64_t t, int64_t* first_bad, uint64_t* bad_count) {
+    *bad_count += 1;
+    if (*first_bad < 0 || t < *first_bad) *first_bad = t;
+}
+
+/*
+ * Scatter copy.  All strides are in bytes except idx_stride (elements).
+ * first_bad is set to -1 and bad_count to 0 on entry.  Returns the number of
+ * rows written.
+ */
+int64_t oracle_copy(const uint8_t* k, const uint8_t* v, uint8_t* k_cache, uint8_t* v_cache,
+                    const void* indices, int idx_is_i64, int64_t idx_stride,
+                    int64_t row_bytes, int64_t k_stride, int64_t v_stride,
+                    int64_t cache_stride, int64_t batch, int64_t size_limit,
+                    int64_t* first_bad, uint64_t* bad_count) {
+    int64_t written = 0;
+    *first_bad = -1;
+    *bad_count = 0;
+    for (int64_t t = 0; t < batch; ++t) {
+        int64_t loc = read_index(indices, idx_is_i64, t * idx_stride);
+        if (loc < 0 || loc >= size_limit) {
+            note_bad(t, first_bad, bad_count);
+            continue;
+        }
+        memcpy(k_cache + loc * cache_stride, k + t * k_stride, (size_t)row_bytes);
+        memcpy(v_cache + loc * cache_stride, v + t * v_stride, (size_t)row_bytes);
+        ++written;
+    }
+    return written;
+}
+
+/* One tensor (K or V) of one token into its paged cache slot. */
+static void store_fp8_row(const uint8_t* src, int64_t s_tok, int64_t s_head, int64_t t,
+                          uint8_t* cache, int64_t s_page, int64_t s_off, int64_t s_chead,
+                          int64_t page, int64_t off, int64_t num_heads, int64_t head_dim,
+                          int src_is_fp16, float inv) {
+    for (int64_t h = 0; h < num_heads; ++h) {
+        for (int64_t d = 0; d < head_dim; ++d) {
+            uint16_t bits;
+            memcpy(&bits, src + t * s_tok + h * s_head + 2 * d, sizeof bits);
+            cache[page * s_page + off * s_off + h * s_chead + d] =
+                quantize_one(bits, src_is_fp16, inv);
+        }
+    }
+}
+
+/*
+ * Fused FP8 paged store.  Input strides in bytes (dim stride is one element),
+ * cache strides in bytes (dim stride is one byte).  inv_k / inv_v are host
+ * pointers to fp32 inverse scales, NULL meaning 1.0.  Returns rows written.
+ */
+int64_t oracle_fp8_paged(const uint8_t* k, const uint8_t* v, uint8_t* k_cache,
+                         uint8_t* v_cache, const void* indices, int idx_is_i64,
+                         int64_t idx_stride, int src_is_fp16, int64_t num_heads,
+                         int64_t head_dim, int64_t k_stride_token, int64_t k_stride_head,
+                         int64_t v_stride_token, int64_t v_stride_head,
+                         int64_t kc_stride_page, int64_t kc_stride_offset,
+                         int64_t kc_stride_head, int64_t vc_stride_page,
+                         int64_t vc_stride_offset, int64_t vc_stride_head, int64_t batch,
+                         int64_t size_limit, int64_t page_size, const float* inv_k,
+                         const float* inv_v, int64_t* first_bad, uint64_t* bad_count) {
+    int64_t written = 0;
+    float ik = inv_k ? *inv_k : 1.0f;
+    float iv = inv_v ? *inv_v : 1.0f;
+    *first_bad = -1;
+    *bad_count = 0;
+    for (int64_t t = 0; t < batch; ++t) {
+        int64_t loc = read_index(indices, idx_is_i64, t * idx_stride);
+        if (loc < 0 || loc >= size_limit) {
+            note_bad(t, first_bad, bad_count);
+            continue;
+        }
+        int64_t page = loc / page_size;
+        int64_t off = loc % page_size;
+        store_fp8_row(k, k_stride_token, k_stride_head, t, k_cache, kc_stride_page,
+                      kc_stride_offset, kc_stride_head, page, off, num_heads, head_dim,
+                      src_is_fp16, ik);
+        store_fp8_row(v, v_stride_token, v_stride_head, t, v_cache, vc_stride_page,
+                      vc_stride_offset, vc_stride_head, page, off, num_heads, head_dim,
+                      src_is_fp16, iv);
+        ++written;
+    }
+    return written;
+}
