@@ -1,0 +1,345 @@
+"""Benchmark of the KV-cache store on one MI355X.
+
+One step = the whole store path once: a scatter copy of the prefill workload
+(32768 tokens, 8 heads x 128 dims bf16, int32 indices into 2^21 slots of
+16-slot pages) followed by a fused FP8 e4m3fn paged store (16384 tokens,
+8 x 128 bf16, inverse scales 1/2.5 and 1/1.7, page 64, 2^21 slots).
+
+Inputs are seeded synthetic data, resident in HBM before timing starts.  Calls
+rotate over disjoint input/index sets (more than the 256 MB last-level
+cache), so the figure is an HBM figure, not a cache figure.  The metric is
+effective bandwidth: algorithmic bytes (K/V rows read + indices read + cache
+rows written, + the two fp32 scales) per second.
+
+Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build measures one
+GPU only.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+KERNEL_SRC = os.path.join(ROOT, "fp8_kv_quantization_amd", "csrc", "kvstore.hip")
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_prefill_copy_fp8_paged.md")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sets", type=int, default=8, help="disjoint input/index sets rotated over")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also launch a plain device copy of this size (counter calibration)")
+    ap.add_argument("--no-decode", action="store_true")
+    return ap.parse_args()
+
+
+def source_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
+
+
+def stored_traffic():
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None
+    text = open(PMC_SUMMARY).read()
+    vals = dict(re.findall(r"^(\w+)\s*=\s*(\S+)\s*$", text, re.M))
+    if vals.get("kernel_source_sha256") != source_sha():
+        return None
+    try:
+        return {k: float(vals[k]) for k in ("copy_fetch_bytes", "copy_write_bytes",
+                                            "fp8_fetch_bytes", "fp8_write_bytes")}
+    except KeyError:
+        return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported by this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp8_kv_quantization_amd as kv
+    import kvgen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    S = args.sets
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    log("generating inputs")
+    c3 = kvgen.workload(3)
+    c4 = kvgen.workload(4)
+    idx3 = kvgen.disjoint_index_sets(c3, S)
+    idx4 = kvgen.disjoint_index_sets(c4, S)
+    # set 0 is the canonical workload's own index set
+    idx3[0] = c3.indices
+    idx4[0] = c4.indices
+    assert len(np.unique(np.concatenate(idx3))) == S * c3.num_tokens
+    assert len(np.unique(np.concatenate(idx4))) == S * c4.num_tokens
+
+    # Rotation sets: distinct device buffers; set s holds set 0's rows rolled
+    # by s*997 tokens (same values, different memory).
+    k3 = [to_dev(c3.k)]
+    v3 = [to_dev(c3.v)]
+    k4 = [to_dev(c4.k)]
+    v4 = [to_dev(c4.v)]
+    for s in range(1, S):
+        k3.append(torch.roll(k3[0], s * 997, 0).contiguous())
+        v3.append(torch.roll(v3[0], s * 997, 0).contiguous())
+        k4.append(torch.roll(k4[0], s * 997, 0).contiguous())
+        v4.append(torch.roll(v4[0], s * 997, 0).contiguous())
+    i3 = [to_dev(a) for a in idx3]
+    i4 = [to_dev(a) for a in idx4]
+    inv_k = to_dev(np.array([c4.inv_k_bits], dtype=np.uint32).view(np.float32))
+    inv_v = to_dev(np.array([c4.inv_v_bits], dtype=np.uint32).view(np.float32))
+
+    R3 = c3.row_bytes
+    kc3 = torch.full((c3.slots, R3), 0xFF, dtype=torch.uint8, device=dev)
+    vc3 = torch.full_like(kc3, 0xFF)
+    H, D, P = c4.num_heads, c4.head_dim, c4.page_size
+    R4 = H * D
+    kc4 = torch.full((c4.slots, R4), 0xFF, dtype=torch.uint8, device=dev)
+    vc4 = torch.full_like(kc4, 0xFF)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def copy_call(s):
+        st = kv.kvstore_copy(k3[s].data_ptr(), v3[s].data_ptr(), kc3.data_ptr(), vc3.data_ptr(),
+                             i3[s].data_ptr(), kv.IDX_I32, 1, R3, c3.in_stride_bytes,
+                             c3.in_stride_bytes, R3, c3.num_tokens, c3.slots, sh)
+        if st:
+            raise kv.KVStoreError(st, "kvstore_copy")
+
+    def fp8_call(s):
+        st = kv.kvstore_fp8_paged(
+            k4[s].data_ptr(), v4[s].data_ptr(), kc4.data_ptr(), vc4.data_ptr(), i4[s].data_ptr(),
+            kv.IDX_I32, 1, kv.SRC_BF16, H, D, c4.in_stride_bytes, 2 * D, c4.in_stride_bytes, 2 * D,
+            P * R4, R4, D, P * R4, R4, D, c4.num_tokens, c4.slots, P, inv_k.data_ptr(),
+            inv_v.data_ptr(), sh)
+        if st:
+            raise kv.KVStoreError(st, "kvstore_fp8_paged")
+
+    if args.calib_copy_mib:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+        log(f"calibration copy of {args.calib_copy_mib} MiB launched 3 times")
+
+    log(f"warmup {args.warmup} steps")
+    for i in range(args.warmup):
+        copy_call(i % S)
+        fp8_call(i % S)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K)]
+    log(f"timing {K} steps over {S} rotation sets")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        s = i % S
+        ev[3 * i].record(stream)
+        copy_call(s)
+        ev[3 * i + 1].record(stream)
+        fp8_call(s)
+        ev[3 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    copy_ms = [ev[3 * i].elapsed_time(ev[3 * i + 1]) for i in range(K)]
+    fp8_ms = [ev[3 * i + 1].elapsed_time(ev[3 * i + 2]) for i in range(K)]
+    total_ms = ev[0].elapsed_time(ev[3 * K - 1])
+    ms_per_step = max(total_ms, wall * 1e3) / K
+
+    st, fb, bc = kv.kvstore_check_error(sh)
+    if st != kv.OK:
+        raise RuntimeError(f"device error flag set: first bad token {fb}, count {bc}")
+
+    # Sampled parity on the timed buffers: set 0's slots hold set 0's rows.
+    log("checking set-0 rows against the inputs")
+    rows3 = kc3.index_select(0, i3[0].long())
+    assert torch.equal(rows3, k3[0].view(torch.uint8).view(c3.num_tokens, -1)[:, :R3]), \
+        "prefill copy: cache rows differ from input rows"
+
+    b3 = c3.algorithmic_bytes()
+    b4 = c4.algorithmic_bytes()
+    copy_us = statistics.mean(copy_ms) * 1e3
+    fp8_us = statistics.mean(fp8_ms) * 1e3
+    value = (b3 + b4) / (ms_per_step * 1e-3) / 1e9
+
+    decode = None
+    if not args.no_decode:
+        decode = bench_decode(kv, torch, dev, kvgen, to_dev)
+
+    traffic = stored_traffic()
+    roofline = {
+        "bound": "hbm",
+        "kernel": "kvstore_copy_kernel (prefill copy)",
+        "achieved": round(b3 / (copy_us * 1e-6) / 1e9, 1),
+        "peak": PEAK_HBM_GBS,
+        "unit": "GB/s",
+        "frac": round(b3 / (copy_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "traffic": None if traffic is None else int(traffic["copy_fetch_bytes"] + traffic["copy_write_bytes"]),
+        "algorithmic_bytes": b3,
+        "avg_launch_us": round(copy_us, 3),
+    }
+    breakdown = {
+        "prefill_copy": {"avg_launch_us": round(copy_us, 3), "bytes": b3,
+                         "GB/s": round(b3 / (copy_us * 1e-6) / 1e9, 1),
+                         "frac_of_peak": round(b3 / (copy_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)},
+        "fp8_paged": {"avg_launch_us": round(fp8_us, 3), "bytes": b4,
+                      "GB/s": round(b4 / (fp8_us * 1e-6) / 1e9, 1),
+                      "frac_of_peak": round(b4 / (fp8_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                      "traffic": None if traffic is None else
+                      int(traffic["fp8_fetch_bytes"] + traffic["fp8_write_bytes"])},
+    }
+
+    del k3, v3, k4, v4, kc3, vc3, kc4, vc4
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(c3, c4, args.cpu_reps)
+
+    out = {
+        "metric": "effective HBM GB/s (K/V+idx read + cache write)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic (seeded; inputs resident in HBM; rotated over disjoint sets)",
+        "config": {
+            "workload": "prefill copy (32768 tok, 8x128 bf16, int32, 2^21 slots, 16-slot pages) "
+                        "+ fused FP8 e4m3fn paged store (16384 tok, 8x128 bf16, int32, "
+                        "page 64, 2^21 slots, inv scales 1/2.5 1/1.7)",
+            "bytes_per_step": b3 + b4,
+            "rotation_sets": S,
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "breakdown": breakdown,
+        "decode_copy": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_decode(kv, torch, dev, kvgen, to_dev):
+    """Decode copy (256 tokens, 2 KiB rows, int64, 2^20 slots): per-call time
+    back to back, single-call latency, both from HIP events."""
+    c2 = kvgen.workload(2)
+    S = 16
+    sets = kvgen.disjoint_index_sets(c2, S)
+    sets[0] = c2.indices
+    k = to_dev(c2.k)
+    v = to_dev(c2.v)
+    idx = [to_dev(a) for a in sets]
+    R = c2.row_bytes
+    kc = torch.full((c2.slots, R), 0xFF, dtype=torch.uint8, device=dev)
+    vc = torch.full_like(kc, 0xFF)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def call(s):
+        st = kv.kvstore_copy(k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                             idx[s].data_ptr(), kv.IDX_I64, 1, R, R, R, R, c2.num_tokens,
+                             c2.slots, sh)
+        if st:
+            raise kv.KVStoreError(st, "kvstore_copy")
+
+    for i in range(20):
+        call(i % S)
+    torch.cuda.synchronize()
+    n = 400
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        call(i % S)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    b2b_us = e0.elapsed_time(e1) * 1e3 / n
+    lat = []
+    for i in range(200):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call(i % S)
+        b.record(stream)
+        b.synchronize()
+        lat.append(a.elapsed_time(b) * 1e3)
+    st, _, _ = kv.kvstore_check_error(sh)
+    assert st == kv.OK
+    del kc, vc
+    return {"workload": "decode copy (256 tok, 8x128 bf16, int64, 2^20 slots)",
+            "us_per_call_back_to_back": round(b2b_us, 3),
+            "us_single_call_median": round(statistics.median(lat), 3),
+            "bytes": c2.algorithmic_bytes()}
+
+
+def cpu_baseline(c3, c4, reps):
+    """The CPU oracle (single thread) on the same step: set 0 of both
+    workloads into full-size host caches."""
+    import oracle
+    lib = oracle.load()
+    log("cpu baseline: allocating host caches")
+    kc3 = np.full((c3.slots, c3.row_bytes), 0xFF, dtype=np.uint8)
+    vc3 = np.full_like(kc3, 0xFF)
+    kc4 = np.full((c4.slots, c4.row_elems), 0xFF, dtype=np.uint8)
+    vc4 = np.full_like(kc4, 0xFF)
+    times = []
+    for r in range(reps):
+        t0 = time.perf_counter()
+        oracle.run_case(c3, kc3, vc3, lib=lib)
+        oracle.run_case(c4, kc4, vc4, lib=lib)
+        times.append(time.perf_counter() - t0)
+        log(f"cpu baseline rep {r}: {times[-1]:.3f} s")
+    t = statistics.median(times)
+    b = c3.algorithmic_bytes() + c4.algorithmic_bytes()
+    return {"value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full step (prefill copy 32768 tok + fused FP8 paged 16384 tok, "
+                      f"set 0) into full-size host caches; median of {reps} runs",
+            "seconds_per_step": round(t, 4),
+            "host_cpus": os.cpu_count()}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,260 @@
+"""Python binding of libkvstore, the MI355X (gfx950) KV-cache store.
+
+Argument marshalling only: every step of a store runs in the HIP kernels of
+``libkvstore.so`` (built from ``csrc/kvstore.hip``).  There is no fallback: if
+the library is not built, importing this package raises.
+
+Low level (same names and arguments as the C ABI in ``include/kvstore.h``;
+pointers are ints, strides in bytes unless stated):
+
+    kvstore_copy(...)        -> status
+    kvstore_fp8_paged(...)   -> status
+    kvstore_check_error(stream) -> (status, first_bad_token, bad_count)
+    kvstore_strerror(status) -> str
+
+Tensor level (torch tensors on the GPU; the current stream is used):
+
+    store_kv(k, v, k_cache, v_cache, indices, size_limit=None)
+        sglang "kvcache.cuh" store_kvcache: k/v [T, D] (dim stride 1),
+        caches [S, D] with a shared row stride, indices [T] int32/int64.
+    store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16,
+                       inv_k_scale=None, inv_v_scale=None, size_limit=None)
+        sglang "trtllm_fp8_kv_kernel.py" fused_fp8_set_kv_buffer: k/v
+        [T, H, D] or [T, H*D] bf16/fp16; caches uint8 (e4m3fn bytes) or
+        float8_e4m3fn, flat [slots, H, D] or paged [pages, page_size, H, D];
+        inverse scales as fp32 device tensors (one element) or None.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvstore.so")
+
+OK = 0
+ERR_NULL = -1
+ERR_SHAPE = -2
+ERR_ALIGN = -3
+ERR_DTYPE = -4
+ERR_HIP = -5
+ERR_OOB = -6
+IDX_I32 = 0
+IDX_I64 = 1
+SRC_BF16 = 0
+SRC_FP16 = 1
+
+EXPORTED = ("kvstore_copy", "kvstore_fp8_paged", "kvstore_check_error", "kvstore_strerror")
+
+
+class KVStoreError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {kvstore_strerror(status)} (status {status})" if what
+                         else f"{kvstore_strerror(status)} (status {status})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = C.CDLL(LIB_PATH)
+    vp, i64, i32, u32 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32
+    lib.kvstore_copy.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, u32, i64, vp]
+    lib.kvstore_copy.restype = i32
+    lib.kvstore_fp8_paged.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, C.c_int32, C.c_int32,
+                                      i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, u32, i64,
+                                      i64, vp, vp, vp]
+    lib.kvstore_fp8_paged.restype = i32
+    lib.kvstore_check_error.argtypes = [vp, C.POINTER(C.c_int64), C.POINTER(C.c_uint64)]
+    lib.kvstore_check_error.restype = i32
+    lib.kvstore_strerror.argtypes = [i32]
+    lib.kvstore_strerror.restype = C.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+# ---------------------------------------------------------------------------
+# C ABI, one to one
+# ---------------------------------------------------------------------------
+
+def kvstore_copy(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, row_bytes,
+                 k_stride_bytes, v_stride_bytes, cache_stride_bytes, batch, size_limit,
+                 stream=None) -> int:
+    return _lib.kvstore_copy(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, row_bytes,
+                             k_stride_bytes, v_stride_bytes, cache_stride_bytes, batch,
+                             size_limit, stream)
+
+
+def kvstore_fp8_paged(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype,
+                      num_heads, head_dim, k_stride_token_bytes, k_stride_head_bytes,
+                      v_stride_token_bytes, v_stride_head_bytes, kc_stride_page_bytes,
+                      kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
+                      vc_stride_offset_bytes, vc_stride_head_bytes, batch, size_limit,
+                      page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream=None) -> int:
+    return _lib.kvstore_fp8_paged(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride,
+                                  src_dtype, num_heads, head_dim, k_stride_token_bytes,
+                                  k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
+                                  kc_stride_page_bytes, kc_stride_offset_bytes,
+                                  kc_stride_head_bytes, vc_stride_page_bytes,
+                                  vc_stride_offset_bytes, vc_stride_head_bytes, batch,
+                                  size_limit, page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream)
+
+
+def kvstore_check_error(stream=None):
+    fb = C.c_int64(0)
+    bc = C.c_uint64(0)
+    st = _lib.kvstore_check_error(stream, C.byref(fb), C.byref(bc))
+    return st, fb.value, bc.value
+
+
+def kvstore_strerror(status: int) -> str:
+    return _lib.kvstore_strerror(status).decode()
+
+
+# ---------------------------------------------------------------------------
+# Tensor level
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _idx_code(indices) -> int:
+    torch = _torch()
+    if indices.dtype == torch.int32:
+        return IDX_I32
+    if indices.dtype == torch.int64:
+        return IDX_I64
+    raise TypeError(f"indices must be int32 or int64, got {indices.dtype}")
+
+
+def _check_cuda(*tensors):
+    for t in tensors:
+        if not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def store_kv(k, v, k_cache, v_cache, indices, size_limit=None, stream=None) -> None:
+    """Scatter copy: k_cache[indices[t]] = k[t], v_cache[indices[t]] = v[t]."""
+    _check_cuda(k, v, k_cache, v_cache, indices)
+    if k.dim() != 2 or v.dim() != 2 or k_cache.dim() != 2 or v_cache.dim() != 2:
+        raise ValueError("k, v, k_cache, v_cache must be 2-D")
+    if indices.dim() != 1 or indices.shape[0] != k.shape[0] or v.shape[0] != k.shape[0]:
+        raise ValueError("indices must be [T] with T = k.shape[0] = v.shape[0]")
+    if not (k.dtype == v.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("k, v and the caches must share one dtype")
+    D = k.shape[1]
+    if v.shape[1] != D or k_cache.shape[1] != D or v_cache.shape[1] != D:
+        raise ValueError("row width mismatch")
+    if any(t.stride(1) != 1 for t in (k, v, k_cache, v_cache)):
+        raise ValueError("rows must be contiguous (dim stride 1)")
+    if k_cache.stride(0) != v_cache.stride(0):
+        raise ValueError("k_cache and v_cache must share one row stride")
+    if k_cache.shape[0] != v_cache.shape[0]:
+        raise ValueError("k_cache and v_cache must have the same number of slots")
+    es = k.element_size()
+    limit = k_cache.shape[0] if size_limit is None else int(size_limit)
+    st = kvstore_copy(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                      indices.data_ptr(), _idx_code(indices), indices.stride(0) if k.shape[0] else 1,
+                      D * es, k.stride(0) * es, v.stride(0) * es, k_cache.stride(0) * es,
+                      k.shape[0], limit, _stream_handle(stream))
+    if st != OK:
+        raise KVStoreError(st, "kvstore_copy")
+
+
+def _cache_strides(cache, page_size):
+    """(num_heads, head_dim, slots, (page, offset, head) byte strides) of a
+    flat [slots, H, D] or paged [pages, page_size, H, D] byte cache."""
+    if cache.element_size() != 1:
+        raise TypeError("FP8 caches must be 1-byte elements (uint8 or float8_e4m3fn)")
+    if cache.dim() == 3:
+        slots, H, D = cache.shape
+        if slots % page_size:
+            raise ValueError(f"total_slots ({slots}) must be divisible by page_size ({page_size})")
+        if cache.stride(2) != 1:
+            raise ValueError("cache dim stride must be 1")
+        return H, D, slots, (cache.stride(0) * page_size, cache.stride(0), cache.stride(1))
+    if cache.dim() == 4:
+        pages, ps, H, D = cache.shape
+        if ps != page_size:
+            raise ValueError(f"page_size mismatch: cache has {ps}, expected {page_size}")
+        if cache.stride(3) != 1:
+            raise ValueError("cache dim stride must be 1")
+        return H, D, pages * ps, (cache.stride(0), cache.stride(1), cache.stride(2))
+    raise ValueError(f"Unsupported cache ndim={cache.dim()}, expected 3 or 4")
+
+
+def _input_strides(x, H, D):
+    """(token, head) byte strides of [T, H, D] or [T, H*D] input."""
+    es = x.element_size()
+    if x.dim() == 3:
+        if x.shape[1] != H or x.shape[2] != D:
+            raise ValueError(f"input shape {tuple(x.shape)} does not match cache heads/dim {H}x{D}")
+        if x.stride(2) != 1:
+            raise ValueError("input dim stride must be 1")
+        return x.stride(0) * es, x.stride(1) * es
+    if x.dim() == 2:
+        if x.shape[1] != H * D:
+            raise ValueError(f"input width {x.shape[1]} != {H * D}")
+        if x.stride(1) != 1:
+            raise ValueError("input dim stride must be 1")
+        return x.stride(0) * es, D * es
+    raise ValueError(f"Unsupported input ndim={x.dim()}, expected 2 or 3")
+
+
+def store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16, inv_k_scale=None,
+                       inv_v_scale=None, size_limit=None, stream=None) -> None:
+    """Fused e4m3fn quantise + paged store (scales are fp32 *inverse* scales
+    on the device; None means unscaled)."""
+    torch = _torch()
+    _check_cuda(k, v, k_cache, v_cache, cache_loc)
+    if k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16:
+        src = SRC_BF16
+    elif k.dtype == torch.float16 and v.dtype == torch.float16:
+        src = SRC_FP16
+    else:
+        raise TypeError("k and v must both be bfloat16 or both float16")
+    H, D, slots, kcs = _cache_strides(k_cache, page_size)
+    H2, D2, slots2, vcs = _cache_strides(v_cache, page_size)
+    if (H, D, slots) != (H2, D2, slots2):
+        raise ValueError("k_cache and v_cache shapes differ")
+    ks = _input_strides(k, H, D)
+    vs = _input_strides(v, H, D)
+    T = k.shape[0]
+    if v.shape[0] != T or cache_loc.dim() != 1 or cache_loc.shape[0] != T:
+        raise ValueError("cache_loc must be [T] with T = k.shape[0] = v.shape[0]")
+    ptrs = []
+    for s in (inv_k_scale, inv_v_scale):
+        if s is None:
+            ptrs.append(None)
+            continue
+        if s.dtype != torch.float32 or s.numel() != 1 or not s.is_cuda:
+            raise TypeError("inverse scales must be one-element fp32 GPU tensors")
+        ptrs.append(s.data_ptr())
+    limit = slots if size_limit is None else int(size_limit)
+    st = kvstore_fp8_paged(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                           cache_loc.data_ptr(), _idx_code(cache_loc),
+                           cache_loc.stride(0) if T else 1, src, H, D, ks[0], ks[1], vs[0], vs[1],
+                           kcs[0], kcs[1], kcs[2], vcs[0], vcs[1], vcs[2], T, limit, page_size,
+                           ptrs[0], ptrs[1], _stream_handle(stream))
+    if st != OK:
+        raise KVStoreError(st, "kvstore_fp8_paged")
+
+
+def check_error(stream=None):
+    """(first_bad_token, bad_count) since the last check; (-1, 0) if none.
+    Synchronises the stream."""
+    st, fb, bc = kvstore_check_error(_stream_handle(stream))
+    if st not in (OK, ERR_OOB):
+        raise KVStoreError(st, "kvstore_check_error")
+    return fb, bc

@@ -1,0 +1,519 @@
+// libkvstore: KV-cache store kernels for MI355X (gfx950, CDNA4) and their C ABI.
+//
+// Two operations (declared, with argument rules, in include/kvstore.h):
+//   * kvstore_copy      -- scatter copy of K/V rows into cache slots
+//                          (sglang "kvcache.cuh", store_kvcache).
+//   * kvstore_fp8_paged -- bf16/fp16 -> e4m3fn quantise fused with the paged
+//                          [page, offset, head, dim] write
+//                          (sglang "trtllm_fp8_kv_kernel.py",
+//                          _fused_fp8_set_kv_buffer_kernel).
+//
+// Both are pure data movement, bound by HBM bandwidth; no MFMA and no LDS.
+// Design points for CDNA4:
+//   * one 64-lane wave per (token, slice of the row); each lane moves 16 B per
+//     access (dwordx4), so one wave access covers 1 KiB of a row;
+//   * every load of a wave (K and V, all its 1 KiB chunks) is issued before the
+//     index is needed: the source address does not depend on the index, so the
+//     index fetch overlaps the data fetch instead of preceding it;
+//   * the row base addresses are wave-uniform 64-bit values (scalar registers)
+//     and the per-lane offset is a 32-bit vector register;
+//   * cache rows are written with non-temporal stores (written once, not read
+//     back by this kernel);
+//   * a bad index does not trap: the wave skips its stores and records the
+//     token in a per-device flag (smallest token, count).
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "kvstore.h"
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;                     // lanes per wavefront (CDNA)
+constexpr int kLaneBytes = 16;                // bytes per lane per access
+constexpr int kChunkBytes = kWave * kLaneBytes;  // 1 KiB per wave access
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlockThreads = kWave * kWavesPerBlock;
+constexpr int kMaxChunksPerWave = 4;          // 4 KiB of K + 4 KiB of V in flight per wave
+
+// ---------------------------------------------------------------------------
+// Device error flag (replaces the page's device assert on a bad slot id).
+// ---------------------------------------------------------------------------
+struct DeviceError {
+  unsigned long long first_bad;  // smallest rejected token, ~0 if none
+  unsigned long long bad_count;
+};
+__device__ DeviceError g_kvstore_error = {~0ull, 0ull};
+
+__device__ __forceinline__ void report_bad_token(uint32_t token) {
+  atomicMin(&g_kvstore_error.first_bad, (unsigned long long)token);
+  atomicAdd(&g_kvstore_error.bad_count, 1ull);
+}
+
+__device__ __forceinline__ uint32_t wave_uniform(uint32_t x) {
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+template <typename IdxT>
+__device__ __forceinline__ int64_t load_index(const void* indices, int64_t pos) {
+  return (int64_t)static_cast<const IdxT*>(indices)[pos];
+}
+
+__device__ __forceinline__ u32x4 load16(const uint8_t* base, uint32_t off) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+}
+
+__device__ __forceinline__ void store16(uint8_t* base, uint32_t off, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + off));
+}
+
+// ---------------------------------------------------------------------------
+// Scatter copy.
+// ---------------------------------------------------------------------------
+struct CopyParams {
+  const uint8_t* k;
+  const uint8_t* v;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const void* indices;
+  int64_t idx_stride;
+  int64_t k_stride;
+  int64_t v_stride;
+  int64_t cache_stride;
+  int64_t size_limit;
+  uint32_t row_bytes;
+  uint32_t batch;
+};
+
+// Grid: x = ceil(batch / kWavesPerBlock) blocks of kWavesPerBlock waves, one
+// wave per token; y = slices of the row, kChunks 1 KiB chunks each.
+template <int kChunks, typename IdxT>
+__global__ __launch_bounds__(kBlockThreads) void kvstore_copy_kernel(const CopyParams p) {
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (token >= p.batch) return;
+  const uint32_t slice = blockIdx.y;
+
+  const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
+
+  const uint8_t* ks = p.k + (int64_t)token * p.k_stride;
+  const uint8_t* vs = p.v + (int64_t)token * p.v_stride;
+  const uint32_t col0 = slice * (kChunks * kChunkBytes) + lane * kLaneBytes;
+
+  u32x4 kr[kChunks], vr[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint32_t col = col0 + c * kChunkBytes;
+    if (col < p.row_bytes) {
+      kr[c] = load16(ks, col);
+      vr[c] = load16(vs, col);
+    }
+  }
+
+  if (loc < 0 || loc >= p.size_limit) {
+    if (lane == 0 && slice == 0) report_bad_token(token);
+    return;
+  }
+  uint8_t* kd = p.k_cache + loc * p.cache_stride;
+  uint8_t* vd = p.v_cache + loc * p.cache_stride;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint32_t col = col0 + c * kChunkBytes;
+    if (col < p.row_bytes) {
+      store16(kd, col, kr[c]);
+      store16(vd, col, vr[c]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Fused e4m3fn quantise + paged store.
+// ---------------------------------------------------------------------------
+struct Fp8Params {
+  const uint8_t* k;
+  const uint8_t* v;
+  uint8_t* k_cache;
+  uint8_t* v_cache;
+  const void* indices;
+  const float* inv_k;
+  const float* inv_v;
+  int64_t idx_stride;
+  int64_t k_stride_token, k_stride_head;
+  int64_t v_stride_token, v_stride_head;
+  int64_t kc_stride_page, kc_stride_offset, kc_stride_head;
+  int64_t vc_stride_page, vc_stride_offset, vc_stride_head;
+  int64_t size_limit;
+  int64_t page_size;
+  uint32_t batch;
+  uint32_t units;           // 16-element units per row: num_heads * head_dim / 16
+  uint32_t units_per_head;  // head_dim / 16
+  int32_t page_shift;       // log2(page_size) when a power of two, else -1
+  int32_t linear_pages;     // both caches have page stride == page_size * offset stride
+};
+
+// Exact widening of the two bf16 values packed in a 32-bit word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+}
+
+// fp32 product, then clamp to the largest finite e4m3fn magnitude.  A NaN
+// fails the comparison and passes through; infinities clamp.
+__device__ __forceinline__ float scale_sat(float x, float inv) {
+  const float y = __fmul_rn(x, inv);
+  return (__builtin_fabsf(y) > 448.0f) ? __builtin_copysignf(448.0f, y) : y;
+}
+
+// Four saturated fp32 values -> four e4m3fn bytes (a first in the low byte),
+// with the hardware's round-to-nearest-even packed conversion.
+__device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return (uint32_t)w;
+}
+
+// 16 source elements (two 16-byte vectors) -> 16 e4m3fn bytes.
+template <bool kFp16>
+__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv) {
+  u32x4 out;
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w0 = w[2 * i], w1 = w[2 * i + 1];
+    float e0, e1, e2, e3;
+    if constexpr (kFp16) {
+      e0 = f16_lo(w0); e1 = f16_hi(w0); e2 = f16_lo(w1); e3 = f16_hi(w1);
+    } else {
+      e0 = bf16_lo(w0); e1 = bf16_hi(w0); e2 = bf16_lo(w1); e3 = bf16_hi(w1);
+    }
+    out[i] = pack_e4m3(scale_sat(e0, inv), scale_sat(e1, inv), scale_sat(e2, inv),
+                       scale_sat(e3, inv));
+  }
+  return out;
+}
+
+// Byte offsets of 16-element unit u inside one token's source row and inside
+// one cache slot.  kFlat: heads are back to back in both (offsets linear in u).
+template <bool kFlat>
+__device__ __forceinline__ void unit_offsets(uint32_t u, uint32_t units_per_head,
+                                             int64_t src_head, int64_t dst_head,
+                                             uint32_t* src_off, uint32_t* dst_off) {
+  if constexpr (kFlat) {
+    *src_off = u * 32u;
+    *dst_off = u * 16u;
+  } else {
+    const uint32_t h = u / units_per_head;
+    const uint32_t d = u - h * units_per_head;
+    *src_off = (uint32_t)(h * src_head) + d * 32u;
+    *dst_off = (uint32_t)(h * dst_head) + d * 16u;
+  }
+}
+
+// Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = slices of
+// kPasses * 64 units.  Each lane handles kPasses units of K and of V.
+template <int kPasses, bool kFlat, bool kFp16, typename IdxT>
+__global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const Fp8Params p) {
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (token >= p.batch) return;
+  const uint32_t slice = blockIdx.y;
+
+  const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
+  const float inv_k = p.inv_k ? *p.inv_k : 1.0f;
+  const float inv_v = p.inv_v ? *p.inv_v : 1.0f;
+
+  const uint8_t* ks = p.k + (int64_t)token * p.k_stride_token;
+  const uint8_t* vs = p.v + (int64_t)token * p.v_stride_token;
+
+  u32x4 ka[kPasses], kb[kPasses], va[kPasses], vb[kPasses];
+  uint32_t kdo[kPasses], vdo[kPasses];
+#pragma unroll
+  for (int i = 0; i < kPasses; ++i) {
+    const uint32_t u = (slice * kPasses + i) * kWave + lane;
+    if (u < p.units) {
+      uint32_t kso, vso;
+      unit_offsets<kFlat>(u, p.units_per_head, p.k_stride_head, p.kc_stride_head, &kso, &kdo[i]);
+      unit_offsets<kFlat>(u, p.units_per_head, p.v_stride_head, p.vc_stride_head, &vso, &vdo[i]);
+      ka[i] = load16(ks, kso);
+      kb[i] = load16(ks, kso + 16u);
+      va[i] = load16(vs, vso);
+      vb[i] = load16(vs, vso + 16u);
+    }
+  }
+
+  if (loc < 0 || loc >= p.size_limit) {
+    if (lane == 0 && slice == 0) report_bad_token(token);
+    return;
+  }
+  int64_t k_slot, v_slot;
+  if (p.linear_pages) {
+    k_slot = loc * p.kc_stride_offset;
+    v_slot = loc * p.vc_stride_offset;
+  } else {
+    int64_t page, off;
+    if (p.page_shift >= 0) {
+      page = loc >> p.page_shift;
+      off = loc & (p.page_size - 1);
+    } else {
+      page = loc / p.page_size;
+      off = loc - page * p.page_size;
+    }
+    k_slot = page * p.kc_stride_page + off * p.kc_stride_offset;
+    v_slot = page * p.vc_stride_page + off * p.vc_stride_offset;
+  }
+  uint8_t* kd = p.k_cache + k_slot;
+  uint8_t* vd = p.v_cache + v_slot;
+#pragma unroll
+  for (int i = 0; i < kPasses; ++i) {
+    const uint32_t u = (slice * kPasses + i) * kWave + lane;
+    if (u < p.units) {
+      store16(kd, kdo[i], quantize16<kFp16>(ka[i], kb[i], inv_k));
+      store16(vd, vdo[i], quantize16<kFp16>(va[i], vb[i], inv_v));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Host side: validation, dispatch, launch.
+// ---------------------------------------------------------------------------
+inline bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+inline bool aligned(int64_t s, int64_t a) { return (s % a) == 0; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int64_t kMaxGridY = 65535;
+
+int launch_status() {
+  return hipGetLastError() == hipSuccess ? KVSTORE_OK : KVSTORE_ERR_HIP;
+}
+
+template <typename IdxT>
+int launch_copy(const CopyParams& p, hipStream_t stream) {
+  const int64_t chunks = ceil_div(p.row_bytes, kChunkBytes);
+  const int per_wave = (int)(chunks < kMaxChunksPerWave ? chunks : kMaxChunksPerWave);
+  const int64_t slices = ceil_div(chunks, per_wave);
+  if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
+  const dim3 grid((uint32_t)ceil_div(p.batch, kWavesPerBlock), (uint32_t)slices);
+  const dim3 block(kBlockThreads);
+  switch (per_wave) {
+    case 1: hipLaunchKernelGGL((kvstore_copy_kernel<1, IdxT>), grid, block, 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((kvstore_copy_kernel<2, IdxT>), grid, block, 0, stream, p); break;
+    case 3: hipLaunchKernelGGL((kvstore_copy_kernel<3, IdxT>), grid, block, 0, stream, p); break;
+    default: hipLaunchKernelGGL((kvstore_copy_kernel<4, IdxT>), grid, block, 0, stream, p); break;
+  }
+  return launch_status();
+}
+
+template <int kPasses, bool kFlat, bool kFp16>
+int launch_fp8_idx(const Fp8Params& p, bool i64, dim3 grid, hipStream_t stream) {
+  const dim3 block(kBlockThreads);
+  if (i64)
+    hipLaunchKernelGGL((kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, int64_t>), grid, block,
+                       0, stream, p);
+  else
+    hipLaunchKernelGGL((kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, int32_t>), grid, block,
+                       0, stream, p);
+  return launch_status();
+}
+
+template <int kPasses>
+int launch_fp8_passes(const Fp8Params& p, bool flat, bool fp16, bool i64, dim3 grid,
+                      hipStream_t stream) {
+  if (flat)
+    return fp16 ? launch_fp8_idx<kPasses, true, true>(p, i64, grid, stream)
+                : launch_fp8_idx<kPasses, true, false>(p, i64, grid, stream);
+  return fp16 ? launch_fp8_idx<kPasses, false, true>(p, i64, grid, stream)
+              : launch_fp8_idx<kPasses, false, false>(p, i64, grid, stream);
+}
+
+// Largest byte offset reached by [0, n) * stride must fit in int64 (stride >= 0).
+bool fits(int64_t n, int64_t stride) {
+  return stride == 0 || n <= INT64_MAX / stride;
+}
+
+// Index type, stride (>= 1, and batch * stride * 8 bytes addressable), alignment.
+int check_index_args(const void* indices, int idx_dtype, int64_t idx_stride, uint32_t batch) {
+  if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
+  if (idx_stride < 1 || idx_stride > INT64_MAX / 8 || !fits(batch, idx_stride * 8))
+    return KVSTORE_ERR_SHAPE;
+  if (!aligned(indices, idx_dtype == KVSTORE_IDX_I64 ? 8 : 4)) return KVSTORE_ERR_ALIGN;
+  return KVSTORE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvstore_copy(const void* k, const void* v, void* k_cache, void* v_cache,
+                 const void* indices, int idx_dtype, int64_t idx_stride, int64_t row_bytes,
+                 int64_t k_stride_bytes, int64_t v_stride_bytes, int64_t cache_stride_bytes,
+                 uint32_t batch, int64_t size_limit, hipStream_t stream) {
+  if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
+  if (batch == 0) return KVSTORE_OK;
+  if (!k || !v || !k_cache || !v_cache || !indices) return KVSTORE_ERR_NULL;
+  if (row_bytes <= 0 || row_bytes > INT32_MAX || row_bytes % kLaneBytes) return KVSTORE_ERR_SHAPE;
+  if (k_stride_bytes < 0 || v_stride_bytes < 0 || cache_stride_bytes < row_bytes)
+    return KVSTORE_ERR_SHAPE;
+  if (size_limit <= 0 || !fits(size_limit, cache_stride_bytes)) return KVSTORE_ERR_SHAPE;
+  if (!fits(batch, k_stride_bytes) || !fits(batch, v_stride_bytes)) return KVSTORE_ERR_SHAPE;
+  const int ic = check_index_args(indices, idx_dtype, idx_stride, batch);
+  if (ic != KVSTORE_OK) return ic;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(k_stride_bytes, 16) || !aligned(v_stride_bytes, 16) ||
+      !aligned(cache_stride_bytes, 16))
+    return KVSTORE_ERR_ALIGN;
+
+  CopyParams p;
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.indices = indices;
+  p.idx_stride = idx_stride;
+  p.k_stride = k_stride_bytes;
+  p.v_stride = v_stride_bytes;
+  p.cache_stride = cache_stride_bytes;
+  p.size_limit = size_limit;
+  p.row_bytes = (uint32_t)row_bytes;
+  p.batch = batch;
+  return idx_dtype == KVSTORE_IDX_I64 ? launch_copy<int64_t>(p, stream)
+                                      : launch_copy<int32_t>(p, stream);
+}
+
+int kvstore_fp8_paged(const void* k, const void* v, void* k_cache, void* v_cache,
+                      const void* indices, int idx_dtype, int64_t idx_stride, int src_dtype,
+                      int32_t num_heads, int32_t head_dim, int64_t k_stride_token_bytes,
+                      int64_t k_stride_head_bytes, int64_t v_stride_token_bytes,
+                      int64_t v_stride_head_bytes, int64_t kc_stride_page_bytes,
+                      int64_t kc_stride_offset_bytes, int64_t kc_stride_head_bytes,
+                      int64_t vc_stride_page_bytes, int64_t vc_stride_offset_bytes,
+                      int64_t vc_stride_head_bytes, uint32_t batch, int64_t size_limit,
+                      int64_t page_size, const float* inv_k_scale_ptr,
+                      const float* inv_v_scale_ptr, hipStream_t stream) {
+  if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
+  if (src_dtype != KVSTORE_SRC_BF16 && src_dtype != KVSTORE_SRC_FP16) return KVSTORE_ERR_DTYPE;
+  if (batch == 0) return KVSTORE_OK;
+  if (!k || !v || !k_cache || !v_cache || !indices) return KVSTORE_ERR_NULL;
+  if (num_heads <= 0 || head_dim <= 0 || head_dim % 16) return KVSTORE_ERR_SHAPE;
+  if (page_size <= 0 || size_limit <= 0) return KVSTORE_ERR_SHAPE;
+  const int64_t strides[10] = {k_stride_token_bytes,   k_stride_head_bytes,
+                               v_stride_token_bytes,   v_stride_head_bytes,
+                               kc_stride_page_bytes,   kc_stride_offset_bytes,
+                               kc_stride_head_bytes,   vc_stride_page_bytes,
+                               vc_stride_offset_bytes, vc_stride_head_bytes};
+  for (int64_t s : strides) {
+    if (s < 0) return KVSTORE_ERR_SHAPE;
+    if (!aligned(s, 16)) return KVSTORE_ERR_ALIGN;
+  }
+  // Per-lane offsets inside one token row / one slot are 32-bit.
+  const int64_t heads = num_heads;
+  if ((heads - 1) * k_stride_head_bytes + 2 * (int64_t)head_dim > INT32_MAX ||
+      (heads - 1) * v_stride_head_bytes + 2 * (int64_t)head_dim > INT32_MAX ||
+      (heads - 1) * kc_stride_head_bytes + head_dim > INT32_MAX ||
+      (heads - 1) * vc_stride_head_bytes + head_dim > INT32_MAX)
+    return KVSTORE_ERR_SHAPE;
+  // Largest slot byte offset must fit in int64.
+  const int64_t max_page = (size_limit - 1) / page_size;
+  if (!fits(max_page + 1, kc_stride_page_bytes) || !fits(max_page + 1, vc_stride_page_bytes) ||
+      !fits(page_size, kc_stride_offset_bytes) || !fits(page_size, vc_stride_offset_bytes) ||
+      !fits(size_limit, kc_stride_offset_bytes) || !fits(size_limit, vc_stride_offset_bytes) ||
+      max_page * kc_stride_page_bytes > INT64_MAX - page_size * kc_stride_offset_bytes ||
+      max_page * vc_stride_page_bytes > INT64_MAX - page_size * vc_stride_offset_bytes)
+    return KVSTORE_ERR_SHAPE;
+  if (!fits(batch, k_stride_token_bytes) || !fits(batch, v_stride_token_bytes))
+    return KVSTORE_ERR_SHAPE;
+  const int ic = check_index_args(indices, idx_dtype, idx_stride, batch);
+  if (ic != KVSTORE_OK) return ic;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return KVSTORE_ERR_ALIGN;
+  if (!aligned(inv_k_scale_ptr, 4) || !aligned(inv_v_scale_ptr, 4)) return KVSTORE_ERR_ALIGN;
+
+  Fp8Params p;
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.indices = indices;
+  p.inv_k = inv_k_scale_ptr;
+  p.inv_v = inv_v_scale_ptr;
+  p.idx_stride = idx_stride;
+  p.k_stride_token = k_stride_token_bytes;
+  p.k_stride_head = k_stride_head_bytes;
+  p.v_stride_token = v_stride_token_bytes;
+  p.v_stride_head = v_stride_head_bytes;
+  p.kc_stride_page = kc_stride_page_bytes;
+  p.kc_stride_offset = kc_stride_offset_bytes;
+  p.kc_stride_head = kc_stride_head_bytes;
+  p.vc_stride_page = vc_stride_page_bytes;
+  p.vc_stride_offset = vc_stride_offset_bytes;
+  p.vc_stride_head = vc_stride_head_bytes;
+  p.size_limit = size_limit;
+  p.page_size = page_size;
+  p.batch = batch;
+  p.units_per_head = (uint32_t)(head_dim / 16);
+  const int64_t units = heads * (head_dim / 16);
+  if (units > INT32_MAX) return KVSTORE_ERR_SHAPE;
+  p.units = (uint32_t)units;
+  p.page_shift = -1;
+  if ((page_size & (page_size - 1)) == 0) {
+    int s = 0;
+    while ((int64_t(1) << s) < page_size) ++s;
+    p.page_shift = s;
+  }
+  p.linear_pages = (kc_stride_page_bytes == page_size * kc_stride_offset_bytes &&
+                    vc_stride_page_bytes == page_size * vc_stride_offset_bytes)
+                       ? 1
+                       : 0;
+  const bool flat = k_stride_head_bytes == 2 * (int64_t)head_dim &&
+                    v_stride_head_bytes == 2 * (int64_t)head_dim &&
+                    kc_stride_head_bytes == head_dim && vc_stride_head_bytes == head_dim;
+  const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
+  const bool i64 = idx_dtype == KVSTORE_IDX_I64;
+
+  // Units of 16 elements per lane: up to 2 per lane per tensor in one wave
+  // (32 B of K + 32 B of V loaded per unit), wider rows split over blockIdx.y.
+  const int64_t waves_units = ceil_div(units, kWave);
+  const int passes = waves_units >= 2 ? 2 : 1;
+  const int64_t slices = ceil_div(waves_units, passes);
+  if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
+  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), (uint32_t)slices);
+  return passes == 2 ? launch_fp8_passes<2>(p, flat, fp16, i64, grid, stream)
+                     : launch_fp8_passes<1>(p, flat, fp16, i64, grid, stream);
+}
+
+int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* bad_count) {
+  if (hipStreamSynchronize(stream) != hipSuccess) return KVSTORE_ERR_HIP;
+  DeviceError h;
+  if (hipMemcpyFromSymbol(&h, HIP_SYMBOL(g_kvstore_error), sizeof h, 0,
+                          hipMemcpyDeviceToHost) != hipSuccess)
+    return KVSTORE_ERR_HIP;
+  const DeviceError cleared = {~0ull, 0ull};
+  if (h.bad_count != 0 &&
+      hipMemcpyToSymbol(HIP_SYMBOL(g_kvstore_error), &cleared, sizeof cleared, 0,
+                        hipMemcpyHostToDevice) != hipSuccess)
+    return KVSTORE_ERR_HIP;
+  if (first_bad_token) *first_bad_token = h.bad_count ? (int64_t)h.first_bad : -1;
+  if (bad_count) *bad_count = h.bad_count;
+  return h.bad_count ? KVSTORE_ERR_OOB : KVSTORE_OK;
+}
+
+const char* kvstore_strerror(int status) {
+  switch (status) {
+    case KVSTORE_OK: return "ok";
+    case KVSTORE_ERR_NULL: return "a required pointer is NULL";
+    case KVSTORE_ERR_SHAPE: return "a size or stride is out of range";
+    case KVSTORE_ERR_ALIGN: return "a pointer or stride is not aligned as required";
+    case KVSTORE_ERR_DTYPE: return "unknown index or source type";
+    case KVSTORE_ERR_HIP: return "HIP runtime error";
+    case KVSTORE_ERR_OOB: return "an index was outside [0, size_limit); its row was skipped";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

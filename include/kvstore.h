@@ -1,0 +1,162 @@
+/*
+ * libkvstore -- KV-cache store for MI355X (gfx950).
+ *
+ * Two store operations and their error reporting, as a plain C ABI.  Every
+ * pointer argument of a store call is a DEVICE pointer owned by the caller
+ * (for example a torch tensor's data pointer); the library never allocates,
+ * frees or synchronises inside a store call.  Work is enqueued on the given
+ * HIP stream of the current device and returns immediately, so store calls
+ * may be captured into a HIP graph.
+ *
+ * Operations and the passages that define them:
+ *
+ *   kvstore_copy       -- sglang "kvcache.cuh" (JIT elementwise kernel),
+ *                         store_kvcache / copy_kv_warp and the host run():
+ *                         for each token t, the K row and the V row of t are
+ *                         copied byte for byte into row indices[t] of the K
+ *                         and V caches; the index must lie in [0, size_limit).
+ *   kvstore_fp8_paged  -- sglang "trtllm_fp8_kv_kernel.py",
+ *                         _fused_fp8_set_kv_buffer_kernel, _process_kv_tensor
+ *                         and the wrapper fused_fp8_set_kv_buffer: for token t
+ *                         with loc = indices[t], page = loc / page_size and
+ *                         offset = loc % page_size; every element x of K (V)
+ *                         becomes e4m3fn(x * inv_k) (e4m3fn(x * inv_v)) at
+ *                         [page, offset, head, dim] of the K (V) cache.
+ *
+ * Numerics of kvstore_fp8_paged: x (bf16 or fp16) is widened to fp32 exactly,
+ * multiplied once in fp32 (round to nearest) by the inverse scale, and
+ * rounded to the nearest e4m3fn value with ties to even; values beyond +-448
+ * (including infinities) saturate to +-448, NaN stays NaN (0x7F | sign).
+ * The page leaves rounding and overflow of its float8 cast unstated; this is
+ * the reading the library implements, bit-exactly.
+ *
+ * Out-of-range indices: the page's copy kernel asserts on them and its fused
+ * kernel does not check them at all.  Here a token whose index is outside
+ * [0, size_limit) is skipped (neither its K nor its V row is written, every
+ * other token is) and recorded in a per-device error flag, read and cleared
+ * by kvstore_check_error.  Store calls report only argument errors.
+ *
+ * Indices must be unique within one call: two tokens naming the same slot
+ * race, and which one lands is undefined (as on the pages).
+ *
+ * Concurrency: the error flag is one per device and is shared by every store
+ * call on that device; calls may run concurrently on several streams, but a
+ * kvstore_check_error overlapping a store on another stream may attribute or
+ * clear that store's report.
+ */
+#ifndef KVSTORE_H
+#define KVSTORE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Index element types. */
+enum { KVSTORE_IDX_I32 = 0, KVSTORE_IDX_I64 = 1 };
+
+/* Source element types of kvstore_fp8_paged. */
+enum { KVSTORE_SRC_BF16 = 0, KVSTORE_SRC_FP16 = 1 };
+
+/* Status codes.  Negative codes returned by a store call mean nothing was
+ * launched and no memory was touched. */
+enum {
+  KVSTORE_OK = 0,
+  KVSTORE_ERR_NULL = -1,  /* a required pointer is NULL */
+  KVSTORE_ERR_SHAPE = -2, /* a size or stride is out of range */
+  KVSTORE_ERR_ALIGN = -3, /* a pointer or stride breaks the alignment rule */
+  KVSTORE_ERR_DTYPE = -4, /* unknown index or source type code */
+  KVSTORE_ERR_HIP = -5,   /* the HIP runtime reported an error */
+  KVSTORE_ERR_OOB = -6    /* (kvstore_check_error) some index was out of range */
+};
+
+/*
+ * Scatter copy (sglang "kvcache.cuh", store_kvcache).
+ *
+ *   k, v         device, [batch] rows of row_bytes bytes, row t at
+ *                k + t * k_stride_bytes (v likewise).  Read only.
+ *   k_cache,     device, rows of row_bytes bytes at
+ *   v_cache      cache + slot * cache_stride_bytes (one stride for both, as
+ *                on the page).  Written only at the slots named by indices.
+ *   indices      device, element t at indices[t * idx_stride], of type
+ *                idx_dtype (KVSTORE_IDX_I32 / KVSTORE_IDX_I64).
+ *   idx_stride   in elements, >= 1.
+ *   row_bytes    bytes per K (and V) row: > 0, a multiple of 16, < 2^31.
+ *   *_stride_bytes  multiples of 16; k/v strides >= 0,
+ *                cache_stride_bytes >= row_bytes.
+ *   batch        number of tokens; 0 returns KVSTORE_OK and launches nothing.
+ *   size_limit   valid slots are [0, size_limit); > 0, and
+ *                size_limit * cache_stride_bytes must fit in int64.
+ *   stream       HIP stream of the current device (0 = null stream).
+ *
+ * Alignment: k, v, k_cache, v_cache 16-byte aligned; indices aligned to its
+ * element size.  Element data is never interpreted, so any element type works.
+ * Returns KVSTORE_OK or a negative status (nothing launched).
+ */
+int kvstore_copy(const void* k, const void* v, void* k_cache, void* v_cache,
+                 const void* indices, int idx_dtype, int64_t idx_stride,
+                 int64_t row_bytes, int64_t k_stride_bytes, int64_t v_stride_bytes,
+                 int64_t cache_stride_bytes, uint32_t batch, int64_t size_limit,
+                 hipStream_t stream);
+
+/*
+ * Fused FP8 (e4m3fn) quantise + paged store (sglang "trtllm_fp8_kv_kernel.py",
+ * _fused_fp8_set_kv_buffer_kernel).
+ *
+ *   k, v         device, [batch, num_heads, head_dim] elements of src_dtype
+ *                (KVSTORE_SRC_BF16 / KVSTORE_SRC_FP16); element (t, h, d) at
+ *                byte offset t * *_stride_token_bytes + h * *_stride_head_bytes
+ *                + 2 * d (dim stride is one element).  Read only.
+ *   k_cache,     device, e4m3fn bytes; element (page, off, h, d) at byte offset
+ *   v_cache      page * *c_stride_page_bytes + off * *c_stride_offset_bytes
+ *                + h * *c_stride_head_bytes + d.  Both the page's 4-D
+ *                [pages, page_size, H, D] cache and its flat [slots, H, D]
+ *                cache (page stride = page_size * slot stride) are expressed
+ *                this way.
+ *   indices, idx_dtype, idx_stride, batch, size_limit, stream: as in
+ *                kvstore_copy; size_limit is normally num_pages * page_size.
+ *   num_heads    > 0;  head_dim > 0 and a multiple of 16.
+ *   page_size    > 0 (any value; powers of two take a shift).
+ *   inv_k_scale_ptr, inv_v_scale_ptr
+ *                device pointers to one fp32 inverse scale each, or NULL for
+ *                1.0 (no scaling).  Each is independent.  Read on the device,
+ *                so the call never waits on the host.
+ *
+ * Alignment: k, v and their token/head strides 16-byte aligned; k_cache,
+ * v_cache and their page/offset/head strides 16-byte aligned; indices aligned
+ * to its element size; scale pointers 4-byte aligned.  Strides >= 0; the cache
+ * layout must not overlap itself (offset stride >= heads * head stride when
+ * heads are inside a slot is NOT checked: overlapping layouts race).
+ * Returns KVSTORE_OK or a negative status (nothing launched).
+ */
+int kvstore_fp8_paged(const void* k, const void* v, void* k_cache, void* v_cache,
+                      const void* indices, int idx_dtype, int64_t idx_stride, int src_dtype,
+                      int32_t num_heads, int32_t head_dim, int64_t k_stride_token_bytes,
+                      int64_t k_stride_head_bytes, int64_t v_stride_token_bytes,
+                      int64_t v_stride_head_bytes, int64_t kc_stride_page_bytes,
+                      int64_t kc_stride_offset_bytes, int64_t kc_stride_head_bytes,
+                      int64_t vc_stride_page_bytes, int64_t vc_stride_offset_bytes,
+                      int64_t vc_stride_head_bytes, uint32_t batch, int64_t size_limit,
+                      int64_t page_size, const float* inv_k_scale_ptr,
+                      const float* inv_v_scale_ptr, hipStream_t stream);
+
+/*
+ * Waits for `stream`, then reads and clears the current device's error flag.
+ * Returns KVSTORE_OK when no store since the last check saw an out-of-range
+ * index, KVSTORE_ERR_OOB when some did, KVSTORE_ERR_HIP on a runtime error.
+ * first_bad_token (nullable) receives the smallest rejected token position of
+ * any call since the last check, or -1; bad_count (nullable) the number of
+ * rejected tokens.  This is the only call that synchronises.
+ */
+int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* bad_count);
+
+/* Static, human-readable text for a status code. */
+const char* kvstore_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSTORE_H */

@@ -1,0 +1,374 @@
+"""GPU parity: libkvstore (through its C ABI) against the CPU oracle, byte for byte.
+
+Every case fills the device caches and the oracle's host caches with the same
+sentinel (0xFF), runs the same seeded inputs through both, and compares every
+byte of both caches (so untouched slots are checked too).  Cases cover the five
+workloads at full size and at reduced sizes with ragged tails, every 16-bit
+input pattern through the FP8 conversion, row sizes around every 1 KiB
+boundary, strided and paged layouts, out-of-range indices, an empty batch and
+the largest slot of the largest cache.
+"""
+import numpy as np
+import pytest
+import torch
+
+import fp8_kv_quantization_amd as kv
+import kvgen
+import oracle
+from tests import _ref
+from tests._gpu import (DEV, assert_cache_equal, check_flag, run_copy, run_fp8, sentinel_cache,
+                        to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(f"[gpu-case] {msg}", flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _clean_flag():
+    # every test starts and ends with a clear error flag
+    st, _, _ = check_flag()
+    assert st in (kv.OK, kv.ERR_OOB)
+    yield
+    torch.cuda.synchronize()
+
+
+def copy_parity(case):
+    _say(f"copy {case.name} T={case.num_tokens} slots={case.slots} row={case.row_bytes}")
+    kc = sentinel_cache(case.slots, case.row_bytes)
+    vc = sentinel_cache(case.slots, case.row_bytes)
+    assert run_copy(case, kc, vc) == kv.OK
+    assert check_flag() == (kv.OK, -1, 0)
+    okc, ovc, st = oracle.run_case(case)
+    assert st == (case.num_tokens, -1, 0)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
+def fp8_parity(case):
+    _say(f"fp8 {case.name} T={case.num_tokens} slots={case.slots} src={case.src_dtype}")
+    row = case.row_elems
+    kc = sentinel_cache(case.slots, row)
+    vc = sentinel_cache(case.slots, row)
+    assert run_fp8(case, kc, vc) == kv.OK
+    assert check_flag() == (kv.OK, -1, 0)
+    okc, ovc, st = oracle.run_case(case)
+    assert st == (case.num_tokens, -1, 0)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
+# ---------------------------------------------------------------------------
+# Workloads: reduced (several blocks and a ragged tail) and full size
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,tokens,slots", [(1, None, None), (1, 13, 64), (2, 301, 4096),
+                                            (3, 1001, 8192), (5, 333, 2048)])
+def test_copy_workload_reduced(n, tokens, slots):
+    copy_parity(kvgen.workload(n, tokens=tokens, slots=slots))
+
+
+@pytest.mark.parametrize("tokens,slots", [(257, 64 * 64), (1000, 64 * 64)])
+def test_fp8_workload_reduced(tokens, slots):
+    fp8_parity(kvgen.workload(4, tokens=tokens, slots=slots))
+
+
+@pytest.mark.parametrize("n", [2, 3, 5])
+def test_copy_workload_full_size(n):
+    copy_parity(kvgen.workload(n))
+
+
+def test_fp8_workload_full_size():
+    fp8_parity(kvgen.workload(4))
+
+
+# ---------------------------------------------------------------------------
+# The conversion itself: every bf16 / fp16 pattern under each scale
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("src", ["bf16", "fp16"])
+@pytest.mark.parametrize("inv", [None, kvgen.INV_K_BITS, kvgen.INV_V_BITS],
+                         ids=["noscale", "inv_k", "inv_v"])
+def test_fp8_every_input_pattern(src, inv):
+    case = kvgen.all_patterns_case(src, inv_k_bits=inv, inv_v_bits=inv)
+    _say(f"all patterns {src} inv={inv}")
+    row = case.row_elems
+    kc = sentinel_cache(case.slots, row)
+    vc = sentinel_cache(case.slots, row)
+    assert run_fp8(case, kc, vc) == kv.OK
+    okc, ovc, _ = oracle.run_case(case)
+    got_k = kc.cpu().numpy()[:64].reshape(-1)
+    want_k = okc[:64].reshape(-1)
+    bad = np.nonzero(got_k != want_k)[0]
+    if bad.size:
+        pats = case.k.reshape(-1)[bad[:8]]
+        raise AssertionError(
+            f"{bad.size} of 65536 patterns differ; e.g. "
+            + ", ".join(f"0x{int(p):04x}->got 0x{int(g):02x} want 0x{int(w):02x}"
+                        for p, g, w in zip(pats, got_k[bad[:8]], want_k[bad[:8]])))
+    assert_cache_equal(vc, ovc, "v_cache")
+    # and the oracle agrees with the brute-force nearest-value search
+    np.testing.assert_array_equal(want_k, _ref.expected_codes(case.k, src, inv).reshape(-1))
+
+
+# ---------------------------------------------------------------------------
+# Row sizes around every 1 KiB boundary (epilogue, multi-chunk, split rows)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("row_bytes", [16, 112, 256, 1008, 1024, 1040, 1152, 2048, 2064, 3072,
+                                       4096, 4112, 5120, 20480])
+def test_copy_row_sizes(row_bytes):
+    rng = np.random.Generator(np.random.PCG64(row_bytes))
+    T, slots = 203, 600
+    stride = row_bytes + 48                   # padded input rows
+    kb = rng.integers(0, 255, (T, stride), dtype=np.uint8)
+    vb = rng.integers(0, 255, (T, stride), dtype=np.uint8)
+    idx = rng.permutation(slots)[:T].astype(np.int32)
+    case = kvgen.Case(name=f"rows{row_bytes}", kind="copy", src_dtype="bf16", num_tokens=T,
+                      num_heads=1, head_dim=row_bytes // 2, in_stride_elems=stride // 2,
+                      k=kb.view(np.uint16), v=vb.view(np.uint16), indices=idx, idx_dtype="i32",
+                      slots=slots)
+    copy_parity(case)
+
+
+# ---------------------------------------------------------------------------
+# Layouts and options of the fused store
+# ---------------------------------------------------------------------------
+
+def _fp8_case(tokens=300, pages=16, page_size=64, src="bf16", scales=(True, True), i64=False):
+    c = kvgen.workload(4, tokens=tokens, slots=pages * 64)
+    c.src_dtype = src
+    c.inv_k_bits = kvgen.INV_K_BITS if scales[0] else None
+    c.inv_v_bits = kvgen.INV_V_BITS if scales[1] else None
+    if page_size != 64:
+        c.page_size = page_size
+        c.slots = (c.slots // page_size) * page_size
+        keep = c.indices < c.slots
+        c.indices, c.k, c.v = c.indices[keep].copy(), c.k[keep].copy(), c.v[keep].copy()
+        c.num_tokens = int(keep.sum())
+    if i64:
+        c.indices = c.indices.astype(np.int64)
+        c.idx_dtype = "i64"
+    return c
+
+
+@pytest.mark.parametrize("src,scales,i64", [("bf16", (False, False), False),
+                                            ("bf16", (True, False), True),
+                                            ("fp16", (True, True), False),
+                                            ("fp16", (False, True), True)])
+def test_fp8_options(src, scales, i64):
+    fp8_parity(_fp8_case(src=src, scales=scales, i64=i64))
+
+
+@pytest.mark.parametrize("page_size", [48, 16, 1])
+def test_fp8_page_sizes(page_size):
+    fp8_parity(_fp8_case(page_size=page_size))
+
+
+@pytest.mark.parametrize("page_size", [48, 16])
+def test_fp8_padded_layouts(page_size):
+    # Input heads padded (head stride D+8 elements), cache padded after every
+    # head, every slot and every page: exercises the general address path
+    # (non-linear pages, divide or shift, per-unit head/dim split).
+    c = _fp8_case(tokens=250, pages=8, page_size=page_size)
+    H, D, P = c.num_heads, c.head_dim, c.page_size
+    T = c.num_tokens
+    sh_in = D + 8
+    bk = np.full((T, H, sh_in), kvgen.PAD_POISON, dtype=np.uint16)
+    bv = np.full_like(bk, kvgen.PAD_POISON)
+    bk[:, :, :D] = c.k.reshape(T, H, D)
+    bv[:, :, :D] = c.v.reshape(T, H, D)
+    sh, so = D + 32, H * (D + 32) + 64
+    sp = P * so + 4096
+    pages = c.slots // P
+    _say("fp8 padded layouts")
+    kc = torch.full((pages * sp,), 0xFF, dtype=torch.uint8, device=DEV)
+    vc = torch.full_like(kc, 0xFF)
+    assert run_fp8(c, kc, vc, kc_strides=(sp, so, sh), in_strides=(H * sh_in * 2, sh_in * 2),
+                   k_dev=to_dev(bk), v_dev=to_dev(bv)) == kv.OK
+    okc = np.full(pages * sp, 0xFF, dtype=np.uint8)
+    ovc = np.full_like(okc, 0xFF)
+    oracle.fp8_paged(bk, bv, okc, ovc, c.indices, src_dtype=c.src_dtype, num_heads=H, head_dim=D,
+                     k_strides=(H * sh_in * 2, sh_in * 2), v_strides=(H * sh_in * 2, sh_in * 2),
+                     kc_strides=(sp, so, sh), vc_strides=(sp, so, sh), size_limit=c.slots,
+                     page_size=P, inv_k_bits=c.inv_k_bits, inv_v_bits=c.inv_v_bits)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
+@pytest.mark.parametrize("heads,dim", [(1, 16), (3, 48), (8, 64), (2, 576), (16, 128), (40, 128)])
+def test_fp8_head_shapes(heads, dim):
+    # widths below, at and above one wave's 1024 elements, and split rows
+    rng = np.random.Generator(np.random.PCG64(heads * 1000 + dim))
+    T, P, pages = 130, 16, 12
+    x = rng.standard_normal((2, T, heads * dim), dtype=np.float32) * 40
+    bits = kvgen._round_f32_to_bf16_bits(x)
+    idx = rng.permutation(P * pages)[:T].astype(np.int32)
+    c = kvgen.Case(name=f"h{heads}d{dim}", kind="fp8", src_dtype="bf16", num_tokens=T,
+                   num_heads=heads, head_dim=dim, in_stride_elems=heads * dim, k=bits[0],
+                   v=bits[1], indices=idx, idx_dtype="i32", slots=P * pages, page_size=P,
+                   inv_k_bits=kvgen.INV_K_BITS, inv_v_bits=kvgen.INV_V_BITS)
+    fp8_parity(c)
+
+
+def test_fp8_flat_and_paged_tensor_api_agree():
+    # The page's wrapper accepts a flat [slots, H, D] cache and a paged
+    # [pages, page_size, H, D] cache, 2-D and 3-D inputs; all four give the same bytes.
+    c = _fp8_case(tokens=200, pages=8)
+    H, D, P = c.num_heads, c.head_dim, c.page_size
+    k3 = to_dev(c.k).view(torch.bfloat16).view(-1, H, D)
+    v3 = to_dev(c.v).view(torch.bfloat16).view(-1, H, D)
+    idx = to_dev(c.indices)
+    ik = to_dev(np.array([c.inv_k_bits], dtype=np.uint32).view(np.float32))
+    iv = to_dev(np.array([c.inv_v_bits], dtype=np.uint32).view(np.float32))
+    outs = []
+    for flat in (True, False):
+        for two_d in (True, False):
+            kc = sentinel_cache(c.slots, H * D)
+            vc = sentinel_cache(c.slots, H * D)
+            kcv = kc.view(c.slots, H, D) if flat else kc.view(-1, P, H, D)
+            vcv = vc.view(c.slots, H, D) if flat else vc.view(-1, P, H, D)
+            kin = k3.reshape(-1, H * D) if two_d else k3
+            vin = v3.reshape(-1, H * D) if two_d else v3
+            kv.store_kv_fp8_paged(kin, vin, kcv.view(torch.float8_e4m3fn), vcv, idx, page_size=P,
+                                  inv_k_scale=ik, inv_v_scale=iv)
+            outs.append((kc.cpu().numpy(), vc.cpu().numpy()))
+    okc, ovc, _ = oracle.run_case(c)
+    for a, b in outs:
+        np.testing.assert_array_equal(a, okc)
+        np.testing.assert_array_equal(b, ovc)
+
+
+# ---------------------------------------------------------------------------
+# Indices: bounds, stride, empty batch, largest slot
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["copy", "fp8"])
+@pytest.mark.parametrize("i64", [False, True])
+def test_out_of_range_indices_are_skipped_and_reported(kind, i64):
+    c = kvgen.workload(2, tokens=100, slots=512) if kind == "copy" else _fp8_case(100, 8)
+    dt = np.int64 if i64 else np.int32
+    limit = 384                               # caches hold 512 slots; >= 384 are guard slots
+    idx = np.random.Generator(np.random.PCG64(4)).permutation(limit)[:100].astype(dt)
+    info = np.iinfo(dt)
+    bad = {3: -1, 17: limit, 50: info.max, 98: info.min, 99: limit + 100}
+    for t, val in bad.items():
+        idx[t] = val
+    c.indices = idx
+    c.idx_dtype = "i64" if i64 else "i32"
+    row = c.cache_row_bytes
+    _say(f"oob {kind} i64={i64}")
+    kc = sentinel_cache(512, row)
+    vc = sentinel_cache(512, row)
+    st = (run_copy(c, kc, vc, size_limit=limit) if kind == "copy"
+          else run_fp8(c, kc, vc, size_limit=limit))
+    assert st == kv.OK
+    assert check_flag() == (kv.ERR_OOB, 3, len(bad))
+    assert check_flag() == (kv.OK, -1, 0)      # reading clears it
+    okc = np.full((512, row), 0xFF, dtype=np.uint8)
+    ovc = np.full_like(okc, 0xFF)
+    if kind == "copy":
+        ost = oracle.copy(np.ascontiguousarray(c.k).view(np.uint8),
+                          np.ascontiguousarray(c.v).view(np.uint8), okc, ovc, idx,
+                          row_bytes=c.row_bytes, k_stride=c.in_stride_bytes,
+                          v_stride=c.in_stride_bytes, cache_stride=row, size_limit=limit)
+    else:
+        H, D, P = c.num_heads, c.head_dim, c.page_size
+        ost = oracle.fp8_paged(c.k, c.v, okc, ovc, idx, src_dtype=c.src_dtype, num_heads=H,
+                               head_dim=D, k_strides=(c.in_stride_bytes, 2 * D),
+                               v_strides=(c.in_stride_bytes, 2 * D), kc_strides=(P * row, row, D),
+                               vc_strides=(P * row, row, D), size_limit=limit, page_size=P,
+                               inv_k_bits=c.inv_k_bits, inv_v_bits=c.inv_v_bits)
+    assert ost == (100 - len(bad), 3, len(bad))
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
+def test_flag_accumulates_over_calls_until_read():
+    c = kvgen.workload(1)
+    kc = sentinel_cache(c.slots, c.row_bytes)
+    vc = sentinel_cache(c.slots, c.row_bytes)
+    idx = c.indices.copy()
+    idx[9] = -3
+    assert run_copy(c, kc, vc, idx_dev=to_dev(idx)) == kv.OK
+    idx2 = c.indices.copy()
+    idx2[2] = 999
+    idx2[12] = 1000
+    assert run_copy(c, kc, vc, idx_dev=to_dev(idx2)) == kv.OK
+    assert check_flag() == (kv.ERR_OOB, 2, 3)
+
+
+@pytest.mark.parametrize("kind", ["copy", "fp8"])
+def test_index_stride(kind):
+    c = kvgen.workload(3, tokens=500, slots=4096) if kind == "copy" else _fp8_case(500, 16)
+    strided = np.full(c.num_tokens * 3, -1, dtype=c.indices.dtype)
+    strided[::3] = c.indices
+    dev = to_dev(strided)
+    row = c.cache_row_bytes
+    kc = sentinel_cache(c.slots, row)
+    vc = sentinel_cache(c.slots, row)
+    _say(f"index stride {kind}")
+    st = (run_copy(c, kc, vc, idx_dev=dev, idx_stride=3) if kind == "copy"
+          else run_fp8(c, kc, vc, idx_dev=dev, idx_stride=3))
+    assert st == kv.OK
+    assert check_flag() == (kv.OK, -1, 0)
+    okc, ovc, _ = oracle.run_case(c)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
+def test_empty_batch_touches_nothing():
+    c = kvgen.workload(1)
+    kc = sentinel_cache(c.slots, c.row_bytes)
+    vc = sentinel_cache(c.slots, c.row_bytes)
+    assert run_copy(c, kc, vc, batch=0) == kv.OK
+    f = _fp8_case(10, 1)
+    fk = sentinel_cache(f.slots, f.row_elems)
+    fv = sentinel_cache(f.slots, f.row_elems)
+    assert run_fp8(f, fk, fv, batch=0) == kv.OK
+    torch.cuda.synchronize()
+    for t in (kc, vc, fk, fv):
+        assert bool((t == 0xFF).all())
+    assert check_flag() == (kv.OK, -1, 0)
+
+
+def test_copy_largest_slot_of_the_prefill_cache():
+    # 2^21 slots x 2 KiB: the last slot starts 4 GiB - 2 KiB into the cache,
+    # beyond 32-bit offsets.
+    c = kvgen.workload(3, tokens=64)
+    idx = c.indices.copy()
+    idx[0] = c.slots - 1
+    idx[63] = c.slots - 2
+    idx[31] = (c.slots // 2) + 5
+    assert len(set(idx.tolist())) == idx.size
+    c.indices = idx
+    copy_parity(c)
+
+
+def test_fp8_largest_slot_of_the_paged_cache():
+    c = kvgen.workload(4, tokens=64)
+    idx = c.indices.copy()
+    idx[0] = c.slots - 1
+    idx[10] = c.slots - 64
+    assert len(set(idx.tolist())) == idx.size
+    c.indices = idx
+    fp8_parity(c)
+
+
+# ---------------------------------------------------------------------------
+# Tensor-level copy API
+# ---------------------------------------------------------------------------
+
+def test_store_kv_tensor_api():
+    c = kvgen.workload(5, tokens=200, slots=1024)
+    k = to_dev(c.k).view(torch.float16)[:, :c.row_elems]      # strided [T, 576] view
+    v = to_dev(c.v).view(torch.float16)[:, :c.row_elems]
+    kc = torch.full((c.slots, c.row_elems), -1, dtype=torch.int16, device=DEV).view(torch.float16)
+    vc = torch.full((c.slots, c.row_elems), -1, dtype=torch.int16, device=DEV).view(torch.float16)
+    kv.store_kv(k, v, kc, vc, to_dev(c.indices))
+    assert kv.check_error() == (-1, 0)
+    okc, ovc, _ = oracle.run_case(c)
+    np.testing.assert_array_equal(kc.view(torch.uint8).cpu().numpy(), okc)
+    np.testing.assert_array_equal(vc.view(torch.uint8).cpu().numpy(), ovc)
