@@ -99,11 +99,8 @@ def main():
     log("generating inputs")
     c3 = kvgen.workload(3)
     c4 = kvgen.workload(4)
-    idx3 = kvgen.disjoint_index_sets(c3, S)
+    idx3 = kvgen.disjoint_index_sets(c3, S)      # set 0 = the workload's own indices
     idx4 = kvgen.disjoint_index_sets(c4, S)
-    # set 0 is the canonical workload's own index set
-    idx3[0] = c3.indices
-    idx4[0] = c4.indices
     assert len(np.unique(np.concatenate(idx3))) == S * c3.num_tokens
     assert len(np.unique(np.concatenate(idx4))) == S * c4.num_tokens
 
@@ -270,7 +267,6 @@ def bench_decode(kv, torch, dev, kvgen, to_dev):
     c2 = kvgen.workload(2)
     S = 16
     sets = kvgen.disjoint_index_sets(c2, S)
-    sets[0] = c2.indices
     k = to_dev(c2.k)
     v = to_dev(c2.v)
     idx = [to_dev(a) for a in sets]

@@ -171,12 +171,31 @@ __device__ __forceinline__ float scale_sat(float x, float inv) {
   return (__builtin_fabsf(y) > 448.0f) ? __builtin_copysignf(448.0f, y) : y;
 }
 
+// 0x80 in every byte of w that equals 0xFF, 0 elsewhere.  (b & 0x7F) + 1
+// reaches 0x80 only when the low seven bits are all set, and never carries
+// into the next byte.
+__device__ __forceinline__ uint32_t ff_bytes(uint32_t w) {
+  return ((w & 0x7F7F7F7Fu) + 0x01010101u) & w & 0x80808080u;
+}
+
+// Sign bits of four fp32 values, one per byte (bit 7 of byte i = sign of i).
+__device__ __forceinline__ uint32_t sign_bytes(float a, float b, float c, float d) {
+  return (__float_as_uint(a) >> 24) | ((__float_as_uint(b) >> 16) & 0xFF00u) |
+         ((__float_as_uint(c) >> 8) & 0xFF0000u) | (__float_as_uint(d) & 0xFF000000u);
+}
+
 // Four saturated fp32 values -> four e4m3fn bytes (a first in the low byte),
-// with the hardware's round-to-nearest-even packed conversion.
+// with the hardware's round-to-nearest-even packed conversion.  The converter
+// writes every NaN as 0xFF; a NaN keeps its own sign here (0x7F | sign).  The
+// inputs are already clamped to +-448 (at most 0x7E / 0xFE), so a 0xFF byte
+// can only come from a NaN.
 __device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return (uint32_t)w;
+  uint32_t u = (uint32_t)w;
+  const uint32_t nan = ff_bytes(u);
+  if (nan) u ^= nan & ~sign_bytes(a, b, c, d);
+  return u;
 }
 
 // 16 source elements (two 16-byte vectors) -> 16 e4m3fn bytes.

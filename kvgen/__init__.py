@@ -203,27 +203,34 @@ def workload(n: int, *, tokens: Optional[int] = None, slots: Optional[int] = Non
 
 
 def disjoint_index_sets(case: Case, count: int, seed: Optional[int] = None) -> list:
-    """``count`` index arrays for ``case`` that touch pairwise-disjoint slots,
-    drawn by the same scheme (used to rotate through memory when timing)."""
+    """``count`` index arrays for ``case`` over pairwise-disjoint slots, used to
+    rotate through memory when timing.  Set 0 is the workload's own index
+    array; the others are drawn by the same scheme from the slots (or pages)
+    that set 0 leaves free."""
     rng = np.random.Generator(np.random.PCG64((case.seed if seed is None else seed) + 7919))
     T = case.num_tokens
-    dt = np.int32 if case.idx_dtype == I32 else np.int64
+    dt = case.indices.dtype
+    first = case.indices.astype(np.int64)
     page = case.extra.get("index_page", 1)
+    out = [case.indices.copy()]
     if page > 1:
         need = -(-T // page)
-        perm = rng.permutation(case.slots // page).astype(np.int64)
-        if need * count > perm.size:
+        used = np.unique(first // page)
+        free = np.setdiff1d(np.arange(case.slots // page, dtype=np.int64), used)
+        if need * (count - 1) > free.size:
             raise ValueError("not enough pages for disjoint sets")
+        perm = rng.permutation(free)
         t = np.arange(T, dtype=np.int64)
-        out = []
-        for s in range(count):
+        for s in range(count - 1):
             p = perm[s * need:(s + 1) * need]
             out.append((p[t // page] * page + t % page).astype(dt))
         return out
-    if T * count > case.slots:
+    free = np.setdiff1d(np.arange(case.slots, dtype=np.int64), first)
+    if T * (count - 1) > free.size:
         raise ValueError("not enough slots for disjoint sets")
-    perm = rng.permutation(case.slots).astype(np.int64)
-    return [perm[s * T:(s + 1) * T].astype(dt) for s in range(count)]
+    perm = rng.permutation(free)
+    out += [perm[s * T:(s + 1) * T].astype(dt) for s in range(count - 1)]
+    return out
 
 
 def all_patterns_case(src_dtype: str, inv_k_bits=None, inv_v_bits=None) -> Case:
