@@ -17,8 +17,12 @@
 //     index fetch overlaps the data fetch instead of preceding it;
 //   * the row base addresses are wave-uniform 64-bit values (scalar registers)
 //     and the per-lane offset is a 32-bit vector register;
-//   * cache rows are written with non-temporal stores (written once, not read
-//     back by this kernel);
+//   * copy: cache rows are written with non-temporal stores, and residency is
+//     capped near 8 waves per CU (see copy_blocks_per_cu): the rows land at
+//     scattered slots, and fewer concurrent write streams measured faster;
+//   * fp8: the quantised rows are written with the sc1 cache policy through a
+//     per-row buffer descriptor, at full occupancy (the conversion needs the
+//     latency hiding);
 //   * a bad index does not trap: the wave skips its stores and records the
 //     token in a per-device flag (smallest token, count).
 #include <hip/hip_runtime.h>
@@ -34,8 +38,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;                     // lanes per wavefront (CDNA)
 constexpr int kLaneBytes = 16;                // bytes per lane per access
 constexpr int kChunkBytes = kWave * kLaneBytes;  // 1 KiB per wave access
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = 4;             // fp8 kernel
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
+constexpr int kCopyWavesPerBlock = 2;         // copy kernel
+constexpr int kCopyBlockThreads = kWave * kCopyWavesPerBlock;
 constexpr int kMaxChunksPerWave = 4;          // 4 KiB of K + 4 KiB of V in flight per wave
 
 // ---------------------------------------------------------------------------
@@ -69,6 +75,16 @@ __device__ __forceinline__ void store16(uint8_t* base, uint32_t off, u32x4 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + off));
 }
 
+// Raw buffer descriptor over [row, row + 2^31): stride 0, CDNA data format word.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(uint8_t* row) {
+  return __builtin_amdgcn_make_buffer_rsrc(row, 0, 0x7FFFFFFF, 0x00020000);
+}
+
+// 16-byte store with the sc1 cache policy (bit 4 of the buffer cache-policy operand).
+__device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t row, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, row, (int)off, 0, 16);
+}
+
 // ---------------------------------------------------------------------------
 // Scatter copy.
 // ---------------------------------------------------------------------------
@@ -87,12 +103,12 @@ struct CopyParams {
   uint32_t batch;
 };
 
-// Grid: x = ceil(batch / kWavesPerBlock) blocks of kWavesPerBlock waves, one
-// wave per token; y = slices of the row, kChunks 1 KiB chunks each.
+// Grid: x = ceil(batch / kCopyWavesPerBlock) blocks of kCopyWavesPerBlock
+// waves, one wave per token; y = slices of the row, kChunks 1 KiB chunks each.
 template <int kChunks, typename IdxT>
-__global__ __launch_bounds__(kBlockThreads) void kvstore_copy_kernel(const CopyParams p) {
+__global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const CopyParams p) {
   const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  const uint32_t token = wave_uniform(blockIdx.x * kCopyWavesPerBlock + threadIdx.x / kWave);
   if (token >= p.batch) return;
   const uint32_t slice = blockIdx.y;
 
@@ -198,9 +214,51 @@ __device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d
   return u;
 }
 
-// 16 source elements (two 16-byte vectors) -> 16 e4m3fn bytes.
+// True if any of the 16 source elements is a NaN.  Per 16-bit half,
+// (h & 0x7FFF) + bias reaches bit 15 exactly when the magnitude bits exceed
+// those of infinity (bf16 0x7F80, fp16 0x7C00); the sum never carries out of
+// its half.
 template <bool kFp16>
-__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv) {
+__device__ __forceinline__ bool any_nan16(u32x4 a, u32x4 b) {
+  constexpr uint32_t bias = kFp16 ? 0x03FF03FFu : 0x007F007Fu;
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc |= (w[i] & 0x7FFF7FFFu) + bias;
+  return (acc & 0x80008000u) != 0;
+}
+
+// Same result as quantize16 when no product can be NaN (no NaN input, scale
+// finite and non-zero): the clamp is one v_med3_f32 and no NaN fix-up is needed.
+template <bool kFp16>
+__device__ __forceinline__ u32x4 quantize16_no_nan(u32x4 a, u32x4 b, float inv) {
+  u32x4 out;
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w0 = w[2 * i], w1 = w[2 * i + 1];
+    float e0, e1, e2, e3;
+    if constexpr (kFp16) {
+      e0 = f16_lo(w0); e1 = f16_hi(w0); e2 = f16_lo(w1); e3 = f16_hi(w1);
+    } else {
+      e0 = bf16_lo(w0); e1 = bf16_hi(w0); e2 = bf16_lo(w1); e3 = bf16_hi(w1);
+    }
+    e0 = __builtin_amdgcn_fmed3f(__fmul_rn(e0, inv), -448.0f, 448.0f);
+    e1 = __builtin_amdgcn_fmed3f(__fmul_rn(e1, inv), -448.0f, 448.0f);
+    e2 = __builtin_amdgcn_fmed3f(__fmul_rn(e2, inv), -448.0f, 448.0f);
+    e3 = __builtin_amdgcn_fmed3f(__fmul_rn(e3, inv), -448.0f, 448.0f);
+    int q = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+    q = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, q, true);
+    out[i] = (uint32_t)q;
+  }
+  return out;
+}
+
+// 16 source elements (two 16-byte vectors) -> 16 e4m3fn bytes.  scale_ok:
+// the inverse scale is finite and non-zero (wave-uniform).
+template <bool kFp16>
+__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv, bool scale_ok) {
+  if (scale_ok && !any_nan16<kFp16>(a, b)) return quantize16_no_nan<kFp16>(a, b, inv);
   u32x4 out;
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -247,6 +305,10 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
   const float inv_k = p.inv_k ? *p.inv_k : 1.0f;
   const float inv_v = p.inv_v ? *p.inv_v : 1.0f;
+  // v_med3 drops NaN, so the single-instruction clamp is used only when no
+  // product can be NaN: finite, non-zero scale and no NaN input.
+  const bool k_ok = __builtin_fabsf(inv_k) <= 3.40282347e38f && inv_k != 0.0f;
+  const bool v_ok = __builtin_fabsf(inv_v) <= 3.40282347e38f && inv_v != 0.0f;
 
   const uint8_t* ks = p.k + (int64_t)token * p.k_stride_token;
   const uint8_t* vs = p.v + (int64_t)token * p.v_stride_token;
@@ -287,14 +349,14 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
     k_slot = page * p.kc_stride_page + off * p.kc_stride_offset;
     v_slot = page * p.vc_stride_page + off * p.vc_stride_offset;
   }
-  uint8_t* kd = p.k_cache + k_slot;
-  uint8_t* vd = p.v_cache + v_slot;
+  const __amdgpu_buffer_rsrc_t kd = row_rsrc(p.k_cache + k_slot);
+  const __amdgpu_buffer_rsrc_t vd = row_rsrc(p.v_cache + v_slot);
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
     const uint32_t u = (slice * kPasses + i) * kWave + lane;
     if (u < p.units) {
-      store16(kd, kdo[i], quantize16<kFp16>(ka[i], kb[i], inv_k));
-      store16(vd, vdo[i], quantize16<kFp16>(va[i], vb[i], inv_v));
+      store16_sc1(kd, kdo[i], quantize16<kFp16>(ka[i], kb[i], inv_k, k_ok));
+      store16_sc1(vd, vdo[i], quantize16<kFp16>(va[i], vb[i], inv_v, v_ok));
     }
   }
 }
@@ -312,19 +374,46 @@ int launch_status() {
   return hipGetLastError() == hipSuccess ? KVSTORE_OK : KVSTORE_ERR_HIP;
 }
 
+// Resident copy blocks per CU: about 8 waves per CU.  The copy writes rows
+// at scattered slots; with every wave slot filled (32 per CU) the scattered
+// write streams measured ~5% slower than with 6-10 waves per CU, which still
+// keep 24-40 KiB of loads in flight per CU.  Rows of one chunk move half the
+// bytes per wave, so they get twice the waves.
+constexpr int copy_blocks_per_cu(int chunks_per_wave) {
+  return (chunks_per_wave == 1 ? 16 : 8) / kCopyWavesPerBlock;
+}
+
+// LDS bytes per CU of the current device (cached per device), 0 if unknown.
+int64_t lds_per_cu() {
+  static int64_t cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess || v <= 0)
+      return 0;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
 template <typename IdxT>
 int launch_copy(const CopyParams& p, hipStream_t stream) {
   const int64_t chunks = ceil_div(p.row_bytes, kChunkBytes);
   const int per_wave = (int)(chunks < kMaxChunksPerWave ? chunks : kMaxChunksPerWave);
   const int64_t slices = ceil_div(chunks, per_wave);
   if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
-  const dim3 grid((uint32_t)ceil_div(p.batch, kWavesPerBlock), (uint32_t)slices);
-  const dim3 block(kBlockThreads);
+  const dim3 grid((uint32_t)ceil_div(p.batch, kCopyWavesPerBlock), (uint32_t)slices);
+  const dim3 block(kCopyBlockThreads);
+  // The kernel uses no LDS; the dynamic allocation only caps residency.
+  const int64_t lds = lds_per_cu();
+  const uint32_t lds_bytes = lds > 0 ? (uint32_t)(lds / copy_blocks_per_cu(per_wave)) : 0;
   switch (per_wave) {
-    case 1: hipLaunchKernelGGL((kvstore_copy_kernel<1, IdxT>), grid, block, 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((kvstore_copy_kernel<2, IdxT>), grid, block, 0, stream, p); break;
-    case 3: hipLaunchKernelGGL((kvstore_copy_kernel<3, IdxT>), grid, block, 0, stream, p); break;
-    default: hipLaunchKernelGGL((kvstore_copy_kernel<4, IdxT>), grid, block, 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((kvstore_copy_kernel<1, IdxT>), grid, block, lds_bytes, stream, p); break;
+    case 2: hipLaunchKernelGGL((kvstore_copy_kernel<2, IdxT>), grid, block, lds_bytes, stream, p); break;
+    case 3: hipLaunchKernelGGL((kvstore_copy_kernel<3, IdxT>), grid, block, lds_bytes, stream, p); break;
+    default: hipLaunchKernelGGL((kvstore_copy_kernel<4, IdxT>), grid, block, lds_bytes, stream, p); break;
   }
   return launch_status();
 }
