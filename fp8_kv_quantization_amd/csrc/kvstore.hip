@@ -181,9 +181,11 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
 }
 
 // fp32 product, then clamp to the largest finite e4m3fn magnitude.  A NaN
-// fails the comparison and passes through; infinities clamp.
+// input is its own product (keeping its sign, whichever operand the multiply
+// would return); a NaN fails the comparison and passes through; infinities
+// clamp.
 __device__ __forceinline__ float scale_sat(float x, float inv) {
-  const float y = __fmul_rn(x, inv);
+  const float y = (x != x) ? x : __fmul_rn(x, inv);
   return (__builtin_fabsf(y) > 448.0f) ? __builtin_copysignf(448.0f, y) : y;
 }
 

@@ -87,14 +87,17 @@ static float src_to_float(uint16_t bits, int src_is_fp16) {
  * exact product has at most 48 significant bits and is exact in binary64;
  * converting it to float is then the single round-to-nearest of an fp32
  * multiply, independent of FMA contraction or x87 excess precision.
- * A NaN operand propagates itself (keeping its sign); a NaN made from two
- * non-NaN operands (inf * 0) is the positive default NaN.
+ * A NaN operand propagates itself (keeping its sign; the input before the
+ * scale).  A NaN made from two non-NaN operands (inf * 0) is the negative
+ * default NaN 0xFFC00000: IEEE 754 leaves its sign open, and an fp32 multiply
+ * in torch on the CPU (the arithmetic of the page's unfused path) returns
+ * that pattern.
  */
 static float mul_f32(float x, float inv) {
     if (isnan(x)) return x;
     if (isnan(inv)) return inv;
     double p = (double)x * (double)inv;
-    if (isnan(p)) return NAN;
+    if (isnan(p)) return -NAN;
     return (float)p;
 }
 

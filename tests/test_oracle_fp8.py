@@ -136,3 +136,24 @@ def test_codes_are_monotone_in_value():
     c = oracle.e4m3fn(y).astype(np.int32)
     assert np.all(np.diff(c) >= 0)
     assert c[0] == 0 and c[-1] == 0x7E
+
+
+def test_nan_rules_of_the_product():
+    # Reading: a NaN input is its own product (its sign kept, whatever the
+    # scale); a NaN scale with a non-NaN input gives that scale's NaN; inf * 0
+    # gives the negative default NaN, as torch's fp32 multiply on the CPU does.
+    lib = oracle.load()
+    f = lambda bits: float(np.array([bits], dtype=np.uint32).view(np.float32)[0])
+    def sgn(x):
+        return int(np.signbit(np.float32(x)))
+    neg_nan, pos_nan = f(0xFFC00000), f(0x7FC00000)
+    for x, inv, want_sign in ((neg_nan, 0.4, 1), (pos_nan, -0.4, 0), (neg_nan, pos_nan, 1),
+                              (pos_nan, neg_nan, 0), (1.5, neg_nan, 1), (1.5, pos_nan, 0),
+                              (float("inf"), 0.0, 1), (float("-inf"), 0.0, 1), (0.0, float("inf"), 1)):
+        y = lib.oracle_mul_f32(x, inv)
+        assert np.isnan(y) and sgn(y) == want_sign, (x, inv, y)
+    codes = oracle.e4m3fn(np.array([neg_nan, pos_nan], dtype=np.float32))
+    assert list(codes) == [0xFF, 0x7F]
+    # the library routine this reading follows
+    t = torch.tensor([float("inf"), float("-inf")]) * torch.tensor([0.0, 0.0])
+    assert all(int(v) & 0xFFFFFFFF == 0xFFC00000 for v in t.view(torch.int32))
