@@ -64,6 +64,11 @@ def _bind(lib):
                                      i64, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                      i64, i64, i64, vp, vp, vp, vp]
     lib.oracle_fp8_paged.restype = i64
+    lib.oracle_fp8_paged_dynamic.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i64, i64,
+                                             i64, i64, i64, i64, i64, i64, i64, i64, i64, i64,
+                                             vp, vp, i64, i64, i64, i64, i64, i64, i32,
+                                             i64, i64, i64, vp, vp]
+    lib.oracle_fp8_paged_dynamic.restype = i64
     return lib
 
 
@@ -154,6 +159,53 @@ def fp8_paged(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.nda
         vc_strides[0], vc_strides[1], vc_strides[2], batch, size_limit, page_size,
         None if ik is None else _ptr(ik), None if iv is None else _ptr(iv), _ptr(fb), _ptr(bc))
     return int(n), int(fb[0]), int(bc[0])
+
+
+def fp8_paged_dynamic(k, v, k_cache, v_cache, indices, k_scales, v_scales, *, src_dtype,
+                      num_heads, head_dim, k_strides, v_strides, kc_strides, vc_strides,
+                      ks_strides, vs_strides, per_head, size_limit, page_size,
+                      batch=None, idx_stride=1, lib=None):
+    """Fused FP8 paged store with dynamic scales.  ks_strides/vs_strides =
+    (page, offset, head) byte strides of the fp32 scale caches (k_scales /
+    v_scales are any host arrays, written as raw bytes).
+    Returns (rows_written, first_bad_token, bad_count)."""
+    lib = lib or load()
+    fb = np.zeros(1, dtype=np.int64)
+    bc = np.zeros(1, dtype=np.uint64)
+    is64 = int(indices.dtype == np.int64)
+    if batch is None:
+        batch = (indices.size + idx_stride - 1) // idx_stride
+    n = lib.oracle_fp8_paged_dynamic(
+        _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(indices), is64, idx_stride,
+        int(src_dtype == "fp16"), num_heads, head_dim, k_strides[0], k_strides[1],
+        v_strides[0], v_strides[1], kc_strides[0], kc_strides[1], kc_strides[2],
+        vc_strides[0], vc_strides[1], vc_strides[2], _ptr(k_scales), _ptr(v_scales),
+        ks_strides[0], ks_strides[1], ks_strides[2], vs_strides[0], vs_strides[1],
+        vs_strides[2], int(bool(per_head)), batch, size_limit, page_size, _ptr(fb), _ptr(bc))
+    return int(n), int(fb[0]), int(bc[0])
+
+
+def run_case_dynamic(case, per_head: bool, lib=None):
+    """Dynamic-scale store of a kvgen fp8 case into contiguous sentinel caches
+    ([slots, H*D] bytes) and contiguous scale caches ([slots, groups] fp32,
+    filled with the 0xFFFFFFFF pattern).  Returns (k_cache, v_cache, k_scales,
+    v_scales, status)."""
+    row = case.cache_row_bytes
+    H, D, P = case.num_heads, case.head_dim, case.page_size
+    G = H if per_head else 1
+    kc = np.full((case.slots, row), 0xFF, dtype=np.uint8)
+    vc = np.full_like(kc, 0xFF)
+    ks = np.full((case.slots, G), 0xFFFFFFFF, dtype=np.uint32)
+    vs = np.full_like(ks, 0xFFFFFFFF)
+    cs = (P * row, row, D)
+    ss = (P * G * 4, G * 4, 4)
+    st = fp8_paged_dynamic(case.k, case.v, kc, vc, case.indices, ks, vs,
+                           src_dtype=case.src_dtype, num_heads=H, head_dim=D,
+                           k_strides=(case.in_stride_bytes, 2 * D),
+                           v_strides=(case.in_stride_bytes, 2 * D), kc_strides=cs,
+                           vc_strides=cs, ks_strides=ss, vs_strides=ss, per_head=per_head,
+                           size_limit=case.slots, page_size=P, lib=lib)
+    return kc, vc, ks, vs, st
 
 
 # --------------------------------------------------------------------------

@@ -29,12 +29,23 @@
  *     taken is round-to-nearest-even with saturation to +-448 (a NaN stays a
  *     NaN and keeps its sign).
  *
+ *   - Dynamic scales (the docstring of "trtllm_fp8_kv_kernel.py" lists
+ *     per-token scale computation among the fused kernel's steps; its code
+ *     only takes a given per-tensor scale).  Reading taken: per group (a
+ *     token's whole K or V row, or one head of it), amax = max |x| with NaN
+ *     ignored, scale = max(amax / 448, 2^-126) in fp32 (the floor, the
+ *     smallest normal float, keeps 1 / scale finite for all-zero and tiny
+ *     groups), and inv = 1 / scale in fp32 as the page's wrapper inverts a
+ *     scale; each element becomes e4m3fn(x * inv) and the fp32 scale is
+ *     stored beside the slot.
+ *
  * Parity pins (all in tests/, CPU only): exhaustive nearest-value search over
  * the decoded e4m3fn table for every bf16 and fp16 pattern, torch's own
  * float8_e4m3fn cast where it does not overflow, hand-derived closed-form
  * values, and store invariants (sentinel, round trip, paged == flat, OOB
  * skip, permutation invariance, brute force on tiny inputs).
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -257,3 +268,96 @@ int64_t oracle_fp8_paged(const uint8_t* k, const uint8_t* v, uint8_t* k_cache,
     }
     return written;
 }
+
+/* ---------------------------------------------------------------------- */
+/* Fused FP8 paged store with dynamic per-token / per-token-head scales.    */
+/* ---------------------------------------------------------------------- */
+
+/* Scale of one group: amax / 448 in fp32, at least the smallest normal float. */
+static float group_scale(float amax) {
+    float scale = amax / 448.0f;
+    if (scale < FLT_MIN) scale = FLT_MIN;
+    return scale;
+}
+
+/* max |x| over heads [h0, h1) of one token row, NaN ignored. */
+static float group_amax(const uint8_t* src, int64_t s_tok, int64_t s_head, int64_t t, int64_t h0,
+                        int64_t h1, int64_t head_dim, int src_is_fp16) {
+    float amax = 0.0f;
+    for (int64_t h = h0; h < h1; ++h) {
+        for (int64_t d = 0; d < head_dim; ++d) {
+            uint16_t bits;
+            memcpy(&bits, src + t * s_tok + h * s_head + 2 * d, sizeof bits);
+            float a = fabsf(src_to_float(bits, src_is_fp16));
+            if (a > amax) amax = a;                 /* false for NaN: ignored */
+        }
+    }
+    return amax;
+}
+
+/*
+ * As oracle_fp8_paged, without given scales: for each valid token and each of
+ * K and V, the groups are the whole row (per_head = 0) or each head
+ * (per_head = 1).  The fp32 scale of group g lands at byte offset
+ * page * s_page + offset * s_offset + g * s_head of k_scales / v_scales.
+ */
+int64_t oracle_fp8_paged_dynamic(const uint8_t* k, const uint8_t* v, uint8_t* k_cache,
+                                 uint8_t* v_cache, const void* indices, int idx_is_i64,
+                                 int64_t idx_stride, int src_is_fp16, int64_t num_heads,
+                                 int64_t head_dim, int64_t k_stride_token, int64_t k_stride_head,
+                                 int64_t v_stride_token, int64_t v_stride_head,
+                                 int64_t kc_stride_page, int64_t kc_stride_offset,
+                                 int64_t kc_stride_head, int64_t vc_stride_page,
+                                 int64_t vc_stride_offset, int64_t vc_stride_head,
+                                 uint8_t* k_scales, uint8_t* v_scales, int64_t ks_stride_page,
+                                 int64_t ks_stride_offset, int64_t ks_stride_head,
+                                 int64_t vs_stride_page, int64_t vs_stride_offset,
+                                 int64_t vs_stride_head, int per_head, int64_t batch,
+                                 int64_t size_limit, int64_t page_size, int64_t* first_bad,
+                                 uint64_t* bad_count) {
+    int64_t written = 0;
+    int64_t groups = per_head ? num_heads : 1;
+    int64_t heads_per_group = per_head ? 1 : num_heads;
+    *first_bad = -1;
+    *bad_count = 0;
+    for (int64_t t = 0; t < batch; ++t) {
+        int64_t loc = read_index(indices, idx_is_i64, t * idx_stride);
+        if (loc < 0 || loc >= size_limit) {
+            note_bad(t, first_bad, bad_count);
+            continue;
+        }
+        int64_t page = loc / page_size;
+        int64_t off = loc % page_size;
+        for (int x = 0; x < 2; ++x) {
+            const uint8_t* src = x ? v : k;
+            int64_t s_tok = x ? v_stride_token : k_stride_token;
+            int64_t s_head = x ? v_stride_head : k_stride_head;
+            uint8_t* cache = x ? v_cache : k_cache;
+            int64_t c_page = x ? vc_stride_page : kc_stride_page;
+            int64_t c_off = x ? vc_stride_offset : kc_stride_offset;
+            int64_t c_head = x ? vc_stride_head : kc_stride_head;
+            uint8_t* scales = x ? v_scales : k_scales;
+            int64_t sc_page = x ? vs_stride_page : ks_stride_page;
+            int64_t sc_off = x ? vs_stride_offset : ks_stride_offset;
+            int64_t sc_head = x ? vs_stride_head : ks_stride_head;
+            for (int64_t g = 0; g < groups; ++g) {
+                int64_t h0 = g * heads_per_group, h1 = h0 + heads_per_group;
+                float amax = group_amax(src, s_tok, s_head, t, h0, h1, head_dim, src_is_fp16);
+                float scale = group_scale(amax);
+                float inv = 1.0f / scale;
+                memcpy(scales + page * sc_page + off * sc_off + g * sc_head, &scale, sizeof scale);
+                for (int64_t h = h0; h < h1; ++h) {
+                    for (int64_t d = 0; d < head_dim; ++d) {
+                        uint16_t bits;
+                        memcpy(&bits, src + t * s_tok + h * s_head + 2 * d, sizeof bits);
+                        cache[page * c_page + off * c_off + h * c_head + d] =
+                            quantize_one(bits, src_is_fp16, inv);
+                    }
+                }
+            }
+        }
+        ++written;
+    }
+    return written;
+}
+

@@ -90,6 +90,20 @@ def _fp8(lib):
     return bool(ok)
 
 
+def _dynamic(lib):
+    c = kvgen.workload(4, tokens=60, slots=2 * 64)
+    c.k[3, :] = 0                                       # an all-zero group
+    ok = True
+    for per_head in (False, True):
+        kc, vc, ks, vs, st = oracle.run_case_dynamic(c, per_head, lib=lib)
+        idx = c.indices.astype(np.int64)
+        for cache, scales, src in ((kc, ks, c.k), (vc, vs, c.v)):
+            codes, sc = _ref.dynamic_expected(src, "bf16", 8, 128, per_head)
+            ok &= st == (60, -1, 0) and np.array_equal(cache[idx], codes) \
+                and np.array_equal(scales[idx], sc.view(np.uint32))
+    return bool(ok)
+
+
 def _decode(lib, src):
     got = np.array([lib.oracle_src_to_float(int(b), int(src == "fp16")) for b in ALL16],
                    dtype=np.float32)
@@ -107,6 +121,7 @@ CHECKS = {
     "exhaustive_fp16_noscale": lambda lib: _exhaustive(lib, "fp16", None),
     "copy_store": _copy,
     "fp8_store": _fp8,
+    "fp8_dynamic": _dynamic,
 }
 
 

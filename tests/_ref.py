@@ -117,3 +117,29 @@ def copy_bruteforce(k_bytes, v_bytes, indices, row_bytes, k_stride, v_stride,
         vc[loc * cache_row: loc * cache_row + row_bytes] = vb[t * v_stride: t * v_stride + row_bytes]
     return (np.frombuffer(bytes(kc), dtype=np.uint8).reshape(slots_total, cache_row),
             np.frombuffer(bytes(vc), dtype=np.uint8).reshape(slots_total, cache_row), bad)
+
+
+# ---------------------------------------------------------------------------
+# Dynamic scales: independent float32 reference
+# ---------------------------------------------------------------------------
+
+def dynamic_expected(bits: np.ndarray, src_dtype: str, num_heads: int, head_dim: int,
+                     per_head: bool):
+    """Per token row (bits [T, H*D]): group amax (NaN ignored) -> scale =
+    max(amax / 448, 2^-126) (float32) -> inv = 1 / scale (float32) -> nearest
+    e4m3fn of x * inv.  Returns (codes [T, H*D] uint8, scales [T, G] float32)."""
+    T = bits.shape[0]
+    x = src_bits_to_f32(bits[:, :num_heads * head_dim], src_dtype).reshape(T, num_heads, head_dim)
+    G = num_heads if per_head else 1
+    xg = x.reshape(T, G, -1)
+    with np.errstate(all="ignore"):
+        amax = np.fmax.reduce(np.abs(xg), axis=2, initial=np.float32(0.0)).astype(np.float32)
+        scale = (amax / np.float32(448.0)).astype(np.float32)
+        scale = np.maximum(scale, np.float32(2.0 ** -126)).astype(np.float32)
+        inv = (np.float32(1.0) / scale).astype(np.float32)
+        y = (xg * inv[:, :, None]).astype(np.float32)
+    # an invalid product (inf * 0) is the negative default NaN
+    bad = np.isnan(y) & ~np.isnan(xg)
+    y[bad] = np.array([0xFFC00000], dtype=np.uint32).view(np.float32)[0]
+    codes = nearest_e4m3fn(y.reshape(T, -1), nan_sign_from=np.where(bad, y, xg).reshape(T, -1))
+    return codes.reshape(T, -1), scale

@@ -42,6 +42,13 @@ MUTANTS = {
     "index_stride_ignored": ("read_index(indices, idx_is_i64, t * idx_stride)",
                              "read_index(indices, idx_is_i64, t)"),
     "first_bad_keeps_max": ("t < *first_bad", "t > *first_bad"),
+    "dyn_no_scale_floor": ("if (scale < FLT_MIN) scale = FLT_MIN;", ""),
+    "dyn_inverse_in_one_step": ("float inv = 1.0f / scale;", "float inv = 448.0f / amax;"),
+    "dyn_signed_amax": ("float a = fabsf(src_to_float(bits, src_is_fp16));",
+                        "float a = src_to_float(bits, src_is_fp16);"),
+    "dyn_wrong_fp8_max": ("float scale = amax / 448.0f;", "float scale = amax / 480.0f;"),
+    "dyn_scale_page_offset_swapped": ("scales + page * sc_page + off * sc_off + g * sc_head",
+                                      "scales + off * sc_page + page * sc_off + g * sc_head"),
 }
 
 
