@@ -50,6 +50,7 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also launch a plain device copy of this size (counter calibration)")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements")
     return ap.parse_args()
 
 
@@ -206,6 +207,10 @@ def main():
     if not args.no_decode:
         decode = bench_decode(kv, torch, dev, kvgen, to_dev)
 
+    next_rows = None
+    if not args.no_next:
+        next_rows = bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh)
+
     traffic = stored_traffic()
     roofline = {
         "bound": "hbm",
@@ -260,9 +265,60 @@ def main():
         "roofline": roofline,
         "breakdown": breakdown,
         "decode_copy": decode,
+        "next_rows": next_rows,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh, n=50):
+    """The fused FP8 store with scales computed in the kernel (per token and
+    per token-head) on the FP8 workload's inputs, rotated like the main step."""
+    H, D, P = c4.num_heads, c4.head_dim, c4.page_size
+    R = H * D
+    dev = k4[0].device
+    kc = torch.full((c4.slots, R), 0xFF, dtype=torch.uint8, device=dev)
+    vc = torch.full_like(kc, 0xFF)
+    out = {}
+    for per_head in (False, True):
+        G = H if per_head else 1
+        ks = torch.zeros((c4.slots, G), dtype=torch.float32, device=dev)
+        vs = torch.zeros_like(ks)
+
+        def call(s):
+            st = kv.kvstore_fp8_paged_dynamic(
+                k4[s].data_ptr(), v4[s].data_ptr(), kc.data_ptr(), vc.data_ptr(), i4[s].data_ptr(),
+                kv.IDX_I32, 1, kv.SRC_BF16, H, D, c4.in_stride_bytes, 2 * D, c4.in_stride_bytes,
+                2 * D, P * R, R, D, P * R, R, D, ks.data_ptr(), vs.data_ptr(),
+                kv.SCALE_PER_TOKEN_HEAD if per_head else kv.SCALE_PER_TOKEN,
+                P * G * 4, G * 4, 4 if per_head else 0, P * G * 4, G * 4, 4 if per_head else 0,
+                c4.num_tokens, c4.slots, P, sh)
+            if st:
+                raise kv.KVStoreError(st, "kvstore_fp8_paged_dynamic")
+
+        for i in range(5):
+            call(i % S)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(torch.cuda.current_stream())
+        for i in range(n):
+            call(i % S)
+        e1.record(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / n
+        T = c4.num_tokens
+        b = 2 * T * 2 * R + T * 4 + 2 * T * R + 2 * T * G * 4
+        out["fp8_dynamic_" + ("per_head" if per_head else "per_token")] = {
+            "workload": "fused FP8 paged store, scales computed per "
+                        + ("token and head" if per_head else "token")
+                        + " (16384 tok, 8x128 bf16, int32, page 64)",
+            "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del ks, vs
+    st, _, _ = kv.kvstore_check_error(sh)
+    assert st == kv.OK
+    del kc, vc
+    return out
 
 
 def bench_decode(kv, torch, dev, kvgen, to_dev):

@@ -9,6 +9,7 @@ pointers are ints, strides in bytes unless stated):
 
     kvstore_copy(...)        -> status
     kvstore_fp8_paged(...)   -> status
+    kvstore_fp8_paged_dynamic(...) -> status
     kvstore_check_error(stream) -> (status, first_bad_token, bad_count)
     kvstore_strerror(status) -> str
 
@@ -23,6 +24,12 @@ Tensor level (torch tensors on the GPU; the current stream is used):
         [T, H, D] or [T, H*D] bf16/fp16; caches uint8 (e4m3fn bytes) or
         float8_e4m3fn, flat [slots, H, D] or paged [pages, page_size, H, D];
         inverse scales as fp32 device tensors (one element) or None.
+    store_kv_fp8_paged_dynamic(k, v, k_cache, v_cache, cache_loc,
+                               k_scale_cache, v_scale_cache, per_head=False,
+                               page_size=16, size_limit=None)
+        the same store with scales computed per token (or per token and head)
+        and written as fp32 into scale caches shaped [slots] / [slots, H]
+        (flat) or [pages, page_size] / [pages, page_size, H] (paged).
 """
 from __future__ import annotations
 
@@ -43,8 +50,11 @@ IDX_I32 = 0
 IDX_I64 = 1
 SRC_BF16 = 0
 SRC_FP16 = 1
+SCALE_PER_TOKEN = 0
+SCALE_PER_TOKEN_HEAD = 1
 
-EXPORTED = ("kvstore_copy", "kvstore_fp8_paged", "kvstore_check_error", "kvstore_strerror")
+EXPORTED = ("kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_dynamic",
+            "kvstore_check_error", "kvstore_strerror")
 
 
 class KVStoreError(RuntimeError):
@@ -66,6 +76,11 @@ def _load():
                                       i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, u32, i64,
                                       i64, vp, vp, vp]
     lib.kvstore_fp8_paged.restype = i32
+    lib.kvstore_fp8_paged_dynamic.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, C.c_int32,
+                                              C.c_int32, i64, i64, i64, i64, i64, i64, i64, i64,
+                                              i64, i64, vp, vp, i32, i64, i64, i64, i64, i64, i64,
+                                              u32, i64, i64, vp]
+    lib.kvstore_fp8_paged_dynamic.restype = i32
     lib.kvstore_check_error.argtypes = [vp, C.POINTER(C.c_int64), C.POINTER(C.c_uint64)]
     lib.kvstore_check_error.restype = i32
     lib.kvstore_strerror.argtypes = [i32]
@@ -101,6 +116,24 @@ def kvstore_fp8_paged(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, sr
                                   kc_stride_head_bytes, vc_stride_page_bytes,
                                   vc_stride_offset_bytes, vc_stride_head_bytes, batch,
                                   size_limit, page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream)
+
+
+def kvstore_fp8_paged_dynamic(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype,
+                              num_heads, head_dim, k_stride_token_bytes, k_stride_head_bytes,
+                              v_stride_token_bytes, v_stride_head_bytes, kc_stride_page_bytes,
+                              kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
+                              vc_stride_offset_bytes, vc_stride_head_bytes, k_scale_cache,
+                              v_scale_cache, granularity, ks_stride_page_bytes,
+                              ks_stride_offset_bytes, ks_stride_head_bytes, vs_stride_page_bytes,
+                              vs_stride_offset_bytes, vs_stride_head_bytes, batch, size_limit,
+                              page_size, stream=None) -> int:
+    return _lib.kvstore_fp8_paged_dynamic(
+        k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype, num_heads, head_dim,
+        k_stride_token_bytes, k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
+        kc_stride_page_bytes, kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
+        vc_stride_offset_bytes, vc_stride_head_bytes, k_scale_cache, v_scale_cache, granularity,
+        ks_stride_page_bytes, ks_stride_offset_bytes, ks_stride_head_bytes, vs_stride_page_bytes,
+        vs_stride_offset_bytes, vs_stride_head_bytes, batch, size_limit, page_size, stream)
 
 
 def kvstore_check_error(stream=None):
@@ -249,6 +282,63 @@ def store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16, inv_k_sc
                            ptrs[0], ptrs[1], _stream_handle(stream))
     if st != OK:
         raise KVStoreError(st, "kvstore_fp8_paged")
+
+
+def _scale_strides(sc, per_head, H, page_size):
+    """(page, offset, head) byte strides of a flat [slots(, H)] or paged
+    [pages, page_size(, H)] fp32 scale cache."""
+    torch = _torch()
+    if sc.dtype != torch.float32 or not sc.is_cuda:
+        raise TypeError("scale caches must be float32 GPU tensors")
+    want = 2 if per_head else 1
+    if sc.dim() == want:                       # flat
+        if per_head and sc.shape[1] != H:
+            raise ValueError("per-head scale cache must be [slots, H]")
+        return (sc.stride(0) * 4 * page_size, sc.stride(0) * 4,
+                sc.stride(1) * 4 if per_head else 0), sc.shape[0]
+    if sc.dim() == want + 1:                   # paged
+        if sc.shape[1] != page_size or (per_head and sc.shape[2] != H):
+            raise ValueError("paged scale cache must be [pages, page_size(, H)]")
+        return (sc.stride(0) * 4, sc.stride(1) * 4,
+                sc.stride(2) * 4 if per_head else 0), sc.shape[0] * page_size
+    raise ValueError("unsupported scale cache shape")
+
+
+def store_kv_fp8_paged_dynamic(k, v, k_cache, v_cache, cache_loc, k_scale_cache, v_scale_cache,
+                               per_head=False, page_size=16, size_limit=None, stream=None) -> None:
+    """Fused e4m3fn quantise + paged store with per-token (or per token and
+    head) scales computed in the kernel and written to the scale caches."""
+    torch = _torch()
+    _check_cuda(k, v, k_cache, v_cache, cache_loc, k_scale_cache, v_scale_cache)
+    if k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16:
+        src = SRC_BF16
+    elif k.dtype == torch.float16 and v.dtype == torch.float16:
+        src = SRC_FP16
+    else:
+        raise TypeError("k and v must both be bfloat16 or both float16")
+    H, D, slots, kcs = _cache_strides(k_cache, page_size)
+    H2, D2, slots2, vcs = _cache_strides(v_cache, page_size)
+    if (H, D, slots) != (H2, D2, slots2):
+        raise ValueError("k_cache and v_cache shapes differ")
+    kss, kslots = _scale_strides(k_scale_cache, per_head, H, page_size)
+    vss, vslots = _scale_strides(v_scale_cache, per_head, H, page_size)
+    if kslots != slots or vslots != slots:
+        raise ValueError("scale caches must cover the same slots as the caches")
+    ks = _input_strides(k, H, D)
+    vs = _input_strides(v, H, D)
+    T = k.shape[0]
+    if v.shape[0] != T or cache_loc.dim() != 1 or cache_loc.shape[0] != T:
+        raise ValueError("cache_loc must be [T] with T = k.shape[0] = v.shape[0]")
+    limit = slots if size_limit is None else int(size_limit)
+    st = kvstore_fp8_paged_dynamic(
+        k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_loc.data_ptr(),
+        _idx_code(cache_loc), cache_loc.stride(0) if T else 1, src, H, D, ks[0], ks[1], vs[0],
+        vs[1], kcs[0], kcs[1], kcs[2], vcs[0], vcs[1], vcs[2], k_scale_cache.data_ptr(),
+        v_scale_cache.data_ptr(), SCALE_PER_TOKEN_HEAD if per_head else SCALE_PER_TOKEN,
+        kss[0], kss[1], kss[2], vss[0], vss[1], vss[2], T, limit, page_size,
+        _stream_handle(stream))
+    if st != OK:
+        raise KVStoreError(st, "kvstore_fp8_paged_dynamic")
 
 
 def check_error(stream=None):

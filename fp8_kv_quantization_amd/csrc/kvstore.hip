@@ -363,6 +363,153 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused e4m3fn quantise + paged store with dynamic scales.
+// ---------------------------------------------------------------------------
+constexpr int kMaxDynPasses = 4;   // whole row in one wave: up to 4096 elements
+
+struct Fp8DynParams {
+  Fp8Params base;                  // inv_k / inv_v unused
+  uint8_t* k_scales;
+  uint8_t* v_scales;
+  int64_t ks_stride_page, ks_stride_offset, ks_stride_head;
+  int64_t vs_stride_page, vs_stride_offset, vs_stride_head;
+  uint32_t group_lanes;            // lanes per scale group: 64 (per token) or head_dim / 16
+  int32_t per_head;
+};
+
+// max |x| over 16 source elements; NaN elements are ignored (fmaxf).
+template <bool kFp16>
+__device__ __forceinline__ float amax16(u32x4 a, u32x4 b) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float lo, hi;
+    if constexpr (kFp16) {
+      lo = f16_lo(w[i]); hi = f16_hi(w[i]);
+    } else {
+      lo = bf16_lo(w[i]); hi = bf16_hi(w[i]);
+    }
+    m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+  }
+  return m;
+}
+
+// Max over aligned groups of `lanes` lanes (a power of two <= 64).
+__device__ __forceinline__ float group_max(float v, uint32_t lanes) {
+  for (uint32_t m = 1; m < lanes; m <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, (int)m));
+  return v;
+}
+
+// fp32 scale of a group, at least the smallest normal float.
+__device__ __forceinline__ float dyn_scale(float amax) {
+  return __builtin_fmaxf(amax / 448.0f, 1.17549435e-38f);
+}
+
+// Grid: x = ceil(batch / kWavesPerBlock), one wave per token holding the
+// whole row: kPasses units of 16 elements per lane for K and for V.
+template <int kPasses, bool kFlat, bool kFp16, typename IdxT>
+__global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(const Fp8DynParams d) {
+  const Fp8Params& p = d.base;
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (token >= p.batch) return;
+
+  const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
+  const uint8_t* ks = p.k + (int64_t)token * p.k_stride_token;
+  const uint8_t* vs = p.v + (int64_t)token * p.v_stride_token;
+
+  u32x4 ka[kPasses], kb[kPasses], va[kPasses], vb[kPasses];
+  uint32_t kdo[kPasses], vdo[kPasses];
+  float km[kPasses], vm[kPasses];
+#pragma unroll
+  for (int i = 0; i < kPasses; ++i) {
+    const uint32_t u = i * kWave + lane;
+    km[i] = 0.0f;
+    vm[i] = 0.0f;
+    if (u < p.units) {
+      uint32_t kso, vso;
+      unit_offsets<kFlat>(u, p.units_per_head, p.k_stride_head, p.kc_stride_head, &kso, &kdo[i]);
+      unit_offsets<kFlat>(u, p.units_per_head, p.v_stride_head, p.vc_stride_head, &vso, &vdo[i]);
+      ka[i] = load16(ks, kso);
+      kb[i] = load16(ks, kso + 16u);
+      va[i] = load16(vs, vso);
+      vb[i] = load16(vs, vso + 16u);
+    }
+  }
+  // Every lane takes part in the shuffles below, so the bounds check comes after.
+#pragma unroll
+  for (int i = 0; i < kPasses; ++i) {
+    const uint32_t u = i * kWave + lane;
+    if (u < p.units) {
+      km[i] = amax16<kFp16>(ka[i], kb[i]);
+      vm[i] = amax16<kFp16>(va[i], vb[i]);
+    }
+  }
+  if (!d.per_head) {
+    // one group: the whole row
+    float mk = km[0], mv = vm[0];
+#pragma unroll
+    for (int i = 1; i < kPasses; ++i) {
+      mk = __builtin_fmaxf(mk, km[i]);
+      mv = __builtin_fmaxf(mv, vm[i]);
+    }
+    mk = group_max(mk, kWave);
+    mv = group_max(mv, kWave);
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+      km[i] = mk;
+      vm[i] = mv;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+      km[i] = group_max(km[i], d.group_lanes);
+      vm[i] = group_max(vm[i], d.group_lanes);
+    }
+  }
+
+  if (loc < 0 || loc >= p.size_limit) {
+    if (lane == 0) report_bad_token(token);
+    return;
+  }
+  int64_t page, off;
+  if (p.page_shift >= 0) {
+    page = loc >> p.page_shift;
+    off = loc & (p.page_size - 1);
+  } else {
+    page = loc / p.page_size;
+    off = loc - page * p.page_size;
+  }
+  const __amdgpu_buffer_rsrc_t kd =
+      row_rsrc(p.k_cache + page * p.kc_stride_page + off * p.kc_stride_offset);
+  const __amdgpu_buffer_rsrc_t vd =
+      row_rsrc(p.v_cache + page * p.vc_stride_page + off * p.vc_stride_offset);
+  uint8_t* kss = d.k_scales + page * d.ks_stride_page + off * d.ks_stride_offset;
+  uint8_t* vss = d.v_scales + page * d.vs_stride_page + off * d.vs_stride_offset;
+#pragma unroll
+  for (int i = 0; i < kPasses; ++i) {
+    const uint32_t u = i * kWave + lane;
+    if (u < p.units) {
+      const float sk = dyn_scale(km[i]), sv = dyn_scale(vm[i]);
+      const float ik = 1.0f / sk, iv = 1.0f / sv;
+      // ik, iv are finite and non-zero unless a group holds an infinity
+      const bool k_ok = ik != 0.0f, v_ok = iv != 0.0f;
+      store16_sc1(kd, kdo[i], quantize16<kFp16>(ka[i], kb[i], ik, k_ok));
+      store16_sc1(vd, vdo[i], quantize16<kFp16>(va[i], vb[i], iv, v_ok));
+      // One lane per group writes its scale: the first lane of each head
+      // (per head, g < num_heads), or unit 0 alone (per token, g = 0).
+      if (d.per_head ? (u & (d.group_lanes - 1)) == 0 : u == 0) {
+        const uint32_t g = d.per_head ? u / d.group_lanes : 0u;
+        *reinterpret_cast<float*>(kss + g * d.ks_stride_head) = sk;
+        *reinterpret_cast<float*>(vss + g * d.vs_stride_head) = sv;
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Host side: validation, dispatch, launch.
 // ---------------------------------------------------------------------------
@@ -442,6 +589,29 @@ int launch_fp8_passes(const Fp8Params& p, bool flat, bool fp16, bool i64, dim3 g
               : launch_fp8_idx<kPasses, false, false>(p, i64, grid, stream);
 }
 
+
+template <int kPasses, bool kFlat, bool kFp16>
+int launch_dyn_idx(const Fp8DynParams& d, bool i64, dim3 grid, hipStream_t stream) {
+  const dim3 block(kBlockThreads);
+  if (i64)
+    hipLaunchKernelGGL((kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, int64_t>), grid, block,
+                       0, stream, d);
+  else
+    hipLaunchKernelGGL((kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, int32_t>), grid, block,
+                       0, stream, d);
+  return launch_status();
+}
+
+template <int kPasses>
+int launch_dyn_passes(const Fp8DynParams& d, bool flat, bool fp16, bool i64, dim3 grid,
+                      hipStream_t stream) {
+  if (flat)
+    return fp16 ? launch_dyn_idx<kPasses, true, true>(d, i64, grid, stream)
+                : launch_dyn_idx<kPasses, true, false>(d, i64, grid, stream);
+  return fp16 ? launch_dyn_idx<kPasses, false, true>(d, i64, grid, stream)
+              : launch_dyn_idx<kPasses, false, false>(d, i64, grid, stream);
+}
+
 // Largest byte offset reached by [0, n) * stride must fit in int64 (stride >= 0).
 bool fits(int64_t n, int64_t stride) {
   return stride == 0 || n <= INT64_MAX / stride;
@@ -454,6 +624,94 @@ int check_index_args(const void* indices, int idx_dtype, int64_t idx_stride, uin
     return KVSTORE_ERR_SHAPE;
   if (!aligned(indices, idx_dtype == KVSTORE_IDX_I64 ? 8 : 4)) return KVSTORE_ERR_ALIGN;
   return KVSTORE_OK;
+}
+
+// Checks the arguments the two fused FP8 stores share and fills p (the scale
+// pointers are left NULL).  Returns KVSTORE_OK or the status to return.
+int fill_fp8_params(Fp8Params& p, const void* k, const void* v, void* k_cache, void* v_cache,
+                    const void* indices, int idx_dtype, int64_t idx_stride, int32_t num_heads,
+                    int32_t head_dim, int64_t k_stride_token_bytes, int64_t k_stride_head_bytes,
+                    int64_t v_stride_token_bytes, int64_t v_stride_head_bytes,
+                    int64_t kc_stride_page_bytes, int64_t kc_stride_offset_bytes,
+                    int64_t kc_stride_head_bytes, int64_t vc_stride_page_bytes,
+                    int64_t vc_stride_offset_bytes, int64_t vc_stride_head_bytes, uint32_t batch,
+                    int64_t size_limit, int64_t page_size) {
+  if (!k || !v || !k_cache || !v_cache || !indices) return KVSTORE_ERR_NULL;
+  if (num_heads <= 0 || head_dim <= 0 || head_dim % 16) return KVSTORE_ERR_SHAPE;
+  if (page_size <= 0 || size_limit <= 0) return KVSTORE_ERR_SHAPE;
+  const int64_t strides[10] = {k_stride_token_bytes,   k_stride_head_bytes,
+                               v_stride_token_bytes,   v_stride_head_bytes,
+                               kc_stride_page_bytes,   kc_stride_offset_bytes,
+                               kc_stride_head_bytes,   vc_stride_page_bytes,
+                               vc_stride_offset_bytes, vc_stride_head_bytes};
+  for (int64_t s : strides) {
+    if (s < 0) return KVSTORE_ERR_SHAPE;
+    if (!aligned(s, 16)) return KVSTORE_ERR_ALIGN;
+  }
+  // Per-lane offsets inside one token row / one slot are 32-bit.
+  const int64_t heads = num_heads;
+  if ((heads - 1) * k_stride_head_bytes + 2 * (int64_t)head_dim > INT32_MAX ||
+      (heads - 1) * v_stride_head_bytes + 2 * (int64_t)head_dim > INT32_MAX ||
+      (heads - 1) * kc_stride_head_bytes + head_dim > INT32_MAX ||
+      (heads - 1) * vc_stride_head_bytes + head_dim > INT32_MAX)
+    return KVSTORE_ERR_SHAPE;
+  // Largest slot byte offset must fit in int64.
+  const int64_t max_page = (size_limit - 1) / page_size;
+  if (!fits(max_page + 1, kc_stride_page_bytes) || !fits(max_page + 1, vc_stride_page_bytes) ||
+      !fits(page_size, kc_stride_offset_bytes) || !fits(page_size, vc_stride_offset_bytes) ||
+      !fits(size_limit, kc_stride_offset_bytes) || !fits(size_limit, vc_stride_offset_bytes) ||
+      max_page * kc_stride_page_bytes > INT64_MAX - page_size * kc_stride_offset_bytes ||
+      max_page * vc_stride_page_bytes > INT64_MAX - page_size * vc_stride_offset_bytes)
+    return KVSTORE_ERR_SHAPE;
+  if (!fits(batch, k_stride_token_bytes) || !fits(batch, v_stride_token_bytes))
+    return KVSTORE_ERR_SHAPE;
+  const int ic = check_index_args(indices, idx_dtype, idx_stride, batch);
+  if (ic != KVSTORE_OK) return ic;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return KVSTORE_ERR_ALIGN;
+  const int64_t units = heads * (head_dim / 16);
+  if (units > INT32_MAX) return KVSTORE_ERR_SHAPE;
+
+  p.k = static_cast<const uint8_t*>(k);
+  p.v = static_cast<const uint8_t*>(v);
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.indices = indices;
+  p.inv_k = nullptr;
+  p.inv_v = nullptr;
+  p.idx_stride = idx_stride;
+  p.k_stride_token = k_stride_token_bytes;
+  p.k_stride_head = k_stride_head_bytes;
+  p.v_stride_token = v_stride_token_bytes;
+  p.v_stride_head = v_stride_head_bytes;
+  p.kc_stride_page = kc_stride_page_bytes;
+  p.kc_stride_offset = kc_stride_offset_bytes;
+  p.kc_stride_head = kc_stride_head_bytes;
+  p.vc_stride_page = vc_stride_page_bytes;
+  p.vc_stride_offset = vc_stride_offset_bytes;
+  p.vc_stride_head = vc_stride_head_bytes;
+  p.size_limit = size_limit;
+  p.page_size = page_size;
+  p.batch = batch;
+  p.units_per_head = (uint32_t)(head_dim / 16);
+  p.units = (uint32_t)units;
+  p.page_shift = -1;
+  if ((page_size & (page_size - 1)) == 0) {
+    int sh = 0;
+    while ((int64_t(1) << sh) < page_size) ++sh;
+    p.page_shift = sh;
+  }
+  p.linear_pages = (kc_stride_page_bytes == page_size * kc_stride_offset_bytes &&
+                    vc_stride_page_bytes == page_size * vc_stride_offset_bytes)
+                       ? 1
+                       : 0;
+  return KVSTORE_OK;
+}
+
+// Heads are back to back in the input rows and in the cache slots.
+bool fp8_flat(const Fp8Params& p, int32_t head_dim) {
+  return p.k_stride_head == 2 * (int64_t)head_dim && p.v_stride_head == 2 * (int64_t)head_dim &&
+         p.kc_stride_head == head_dim && p.vc_stride_head == head_dim;
 }
 
 }  // namespace
@@ -509,92 +767,101 @@ int kvstore_fp8_paged(const void* k, const void* v, void* k_cache, void* v_cache
   if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
   if (src_dtype != KVSTORE_SRC_BF16 && src_dtype != KVSTORE_SRC_FP16) return KVSTORE_ERR_DTYPE;
   if (batch == 0) return KVSTORE_OK;
-  if (!k || !v || !k_cache || !v_cache || !indices) return KVSTORE_ERR_NULL;
-  if (num_heads <= 0 || head_dim <= 0 || head_dim % 16) return KVSTORE_ERR_SHAPE;
-  if (page_size <= 0 || size_limit <= 0) return KVSTORE_ERR_SHAPE;
-  const int64_t strides[10] = {k_stride_token_bytes,   k_stride_head_bytes,
-                               v_stride_token_bytes,   v_stride_head_bytes,
-                               kc_stride_page_bytes,   kc_stride_offset_bytes,
-                               kc_stride_head_bytes,   vc_stride_page_bytes,
-                               vc_stride_offset_bytes, vc_stride_head_bytes};
-  for (int64_t s : strides) {
-    if (s < 0) return KVSTORE_ERR_SHAPE;
-    if (!aligned(s, 16)) return KVSTORE_ERR_ALIGN;
-  }
-  // Per-lane offsets inside one token row / one slot are 32-bit.
-  const int64_t heads = num_heads;
-  if ((heads - 1) * k_stride_head_bytes + 2 * (int64_t)head_dim > INT32_MAX ||
-      (heads - 1) * v_stride_head_bytes + 2 * (int64_t)head_dim > INT32_MAX ||
-      (heads - 1) * kc_stride_head_bytes + head_dim > INT32_MAX ||
-      (heads - 1) * vc_stride_head_bytes + head_dim > INT32_MAX)
-    return KVSTORE_ERR_SHAPE;
-  // Largest slot byte offset must fit in int64.
-  const int64_t max_page = (size_limit - 1) / page_size;
-  if (!fits(max_page + 1, kc_stride_page_bytes) || !fits(max_page + 1, vc_stride_page_bytes) ||
-      !fits(page_size, kc_stride_offset_bytes) || !fits(page_size, vc_stride_offset_bytes) ||
-      !fits(size_limit, kc_stride_offset_bytes) || !fits(size_limit, vc_stride_offset_bytes) ||
-      max_page * kc_stride_page_bytes > INT64_MAX - page_size * kc_stride_offset_bytes ||
-      max_page * vc_stride_page_bytes > INT64_MAX - page_size * vc_stride_offset_bytes)
-    return KVSTORE_ERR_SHAPE;
-  if (!fits(batch, k_stride_token_bytes) || !fits(batch, v_stride_token_bytes))
-    return KVSTORE_ERR_SHAPE;
-  const int ic = check_index_args(indices, idx_dtype, idx_stride, batch);
-  if (ic != KVSTORE_OK) return ic;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16))
-    return KVSTORE_ERR_ALIGN;
-  if (!aligned(inv_k_scale_ptr, 4) || !aligned(inv_v_scale_ptr, 4)) return KVSTORE_ERR_ALIGN;
-
   Fp8Params p;
-  p.k = static_cast<const uint8_t*>(k);
-  p.v = static_cast<const uint8_t*>(v);
-  p.k_cache = static_cast<uint8_t*>(k_cache);
-  p.v_cache = static_cast<uint8_t*>(v_cache);
-  p.indices = indices;
+  const int st = fill_fp8_params(
+      p, k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, num_heads, head_dim,
+      k_stride_token_bytes, k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
+      kc_stride_page_bytes, kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
+      vc_stride_offset_bytes, vc_stride_head_bytes, batch, size_limit, page_size);
+  if (st != KVSTORE_OK) return st;
+  if (!aligned(inv_k_scale_ptr, 4) || !aligned(inv_v_scale_ptr, 4)) return KVSTORE_ERR_ALIGN;
   p.inv_k = inv_k_scale_ptr;
   p.inv_v = inv_v_scale_ptr;
-  p.idx_stride = idx_stride;
-  p.k_stride_token = k_stride_token_bytes;
-  p.k_stride_head = k_stride_head_bytes;
-  p.v_stride_token = v_stride_token_bytes;
-  p.v_stride_head = v_stride_head_bytes;
-  p.kc_stride_page = kc_stride_page_bytes;
-  p.kc_stride_offset = kc_stride_offset_bytes;
-  p.kc_stride_head = kc_stride_head_bytes;
-  p.vc_stride_page = vc_stride_page_bytes;
-  p.vc_stride_offset = vc_stride_offset_bytes;
-  p.vc_stride_head = vc_stride_head_bytes;
-  p.size_limit = size_limit;
-  p.page_size = page_size;
-  p.batch = batch;
-  p.units_per_head = (uint32_t)(head_dim / 16);
-  const int64_t units = heads * (head_dim / 16);
-  if (units > INT32_MAX) return KVSTORE_ERR_SHAPE;
-  p.units = (uint32_t)units;
-  p.page_shift = -1;
-  if ((page_size & (page_size - 1)) == 0) {
-    int s = 0;
-    while ((int64_t(1) << s) < page_size) ++s;
-    p.page_shift = s;
-  }
-  p.linear_pages = (kc_stride_page_bytes == page_size * kc_stride_offset_bytes &&
-                    vc_stride_page_bytes == page_size * vc_stride_offset_bytes)
-                       ? 1
-                       : 0;
-  const bool flat = k_stride_head_bytes == 2 * (int64_t)head_dim &&
-                    v_stride_head_bytes == 2 * (int64_t)head_dim &&
-                    kc_stride_head_bytes == head_dim && vc_stride_head_bytes == head_dim;
+  const bool flat = fp8_flat(p, head_dim);
   const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
   const bool i64 = idx_dtype == KVSTORE_IDX_I64;
 
   // Units of 16 elements per lane: up to 2 per lane per tensor in one wave
   // (32 B of K + 32 B of V loaded per unit), wider rows split over blockIdx.y.
-  const int64_t waves_units = ceil_div(units, kWave);
+  const int64_t waves_units = ceil_div(p.units, kWave);
   const int passes = waves_units >= 2 ? 2 : 1;
   const int64_t slices = ceil_div(waves_units, passes);
   if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
   const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), (uint32_t)slices);
   return passes == 2 ? launch_fp8_passes<2>(p, flat, fp16, i64, grid, stream)
                      : launch_fp8_passes<1>(p, flat, fp16, i64, grid, stream);
+}
+
+int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const void* indices, int idx_dtype, int64_t idx_stride,
+                              int src_dtype, int32_t num_heads, int32_t head_dim,
+                              int64_t k_stride_token_bytes, int64_t k_stride_head_bytes,
+                              int64_t v_stride_token_bytes, int64_t v_stride_head_bytes,
+                              int64_t kc_stride_page_bytes, int64_t kc_stride_offset_bytes,
+                              int64_t kc_stride_head_bytes, int64_t vc_stride_page_bytes,
+                              int64_t vc_stride_offset_bytes, int64_t vc_stride_head_bytes,
+                              float* k_scale_cache, float* v_scale_cache, int granularity,
+                              int64_t ks_stride_page_bytes, int64_t ks_stride_offset_bytes,
+                              int64_t ks_stride_head_bytes, int64_t vs_stride_page_bytes,
+                              int64_t vs_stride_offset_bytes, int64_t vs_stride_head_bytes,
+                              uint32_t batch, int64_t size_limit, int64_t page_size,
+                              hipStream_t stream) {
+  if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
+  if (src_dtype != KVSTORE_SRC_BF16 && src_dtype != KVSTORE_SRC_FP16) return KVSTORE_ERR_DTYPE;
+  if (granularity != KVSTORE_SCALE_PER_TOKEN && granularity != KVSTORE_SCALE_PER_TOKEN_HEAD)
+    return KVSTORE_ERR_DTYPE;
+  if (batch == 0) return KVSTORE_OK;
+  Fp8DynParams d;
+  const int st = fill_fp8_params(
+      d.base, k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, num_heads, head_dim,
+      k_stride_token_bytes, k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
+      kc_stride_page_bytes, kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
+      vc_stride_offset_bytes, vc_stride_head_bytes, batch, size_limit, page_size);
+  if (st != KVSTORE_OK) return st;
+  if (!k_scale_cache || !v_scale_cache) return KVSTORE_ERR_NULL;
+  const bool per_head = granularity == KVSTORE_SCALE_PER_TOKEN_HEAD;
+  // The whole row must sit in one wave: at most kMaxDynPasses * 64 units.
+  if (d.base.units > (uint32_t)(kMaxDynPasses * kWave)) return KVSTORE_ERR_SHAPE;
+  // Per-head groups are reduced within aligned lane groups.
+  const uint32_t uph = d.base.units_per_head;
+  if (per_head && (uph > (uint32_t)kWave || (uph & (uph - 1)) != 0)) return KVSTORE_ERR_SHAPE;
+  const int64_t sstrides[6] = {ks_stride_page_bytes, ks_stride_offset_bytes,
+                               ks_stride_head_bytes, vs_stride_page_bytes,
+                               vs_stride_offset_bytes, vs_stride_head_bytes};
+  for (int64_t s : sstrides) {
+    if (s < 0) return KVSTORE_ERR_SHAPE;
+    if (!aligned(s, 4)) return KVSTORE_ERR_ALIGN;
+  }
+  if (!aligned(k_scale_cache, 4) || !aligned(v_scale_cache, 4)) return KVSTORE_ERR_ALIGN;
+  const int64_t groups = per_head ? num_heads : 1;
+  const int64_t max_page = (size_limit - 1) / page_size;
+  if (!fits(max_page + 1, ks_stride_page_bytes) || !fits(max_page + 1, vs_stride_page_bytes) ||
+      !fits(page_size, ks_stride_offset_bytes) || !fits(page_size, vs_stride_offset_bytes) ||
+      !fits(groups, ks_stride_head_bytes) || !fits(groups, vs_stride_head_bytes) ||
+      max_page * ks_stride_page_bytes > INT64_MAX / 2 - page_size * ks_stride_offset_bytes -
+                                            groups * ks_stride_head_bytes ||
+      max_page * vs_stride_page_bytes > INT64_MAX / 2 - page_size * vs_stride_offset_bytes -
+                                            groups * vs_stride_head_bytes)
+    return KVSTORE_ERR_SHAPE;
+
+  d.k_scales = reinterpret_cast<uint8_t*>(k_scale_cache);
+  d.v_scales = reinterpret_cast<uint8_t*>(v_scale_cache);
+  d.ks_stride_page = ks_stride_page_bytes;
+  d.ks_stride_offset = ks_stride_offset_bytes;
+  d.ks_stride_head = ks_stride_head_bytes;
+  d.vs_stride_page = vs_stride_page_bytes;
+  d.vs_stride_offset = vs_stride_offset_bytes;
+  d.vs_stride_head = vs_stride_head_bytes;
+  d.group_lanes = per_head ? uph : (uint32_t)kWave;
+  d.per_head = per_head ? 1 : 0;
+  const bool flat = fp8_flat(d.base, head_dim);
+  const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
+  const bool i64 = idx_dtype == KVSTORE_IDX_I64;
+  const int64_t waves_units = ceil_div(d.base.units, kWave);
+  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock));
+  if (waves_units <= 1) return launch_dyn_passes<1>(d, flat, fp16, i64, grid, stream);
+  if (waves_units <= 2) return launch_dyn_passes<2>(d, flat, fp16, i64, grid, stream);
+  return launch_dyn_passes<4>(d, flat, fp16, i64, grid, stream);
 }
 
 int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* bad_count) {

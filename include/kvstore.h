@@ -1,7 +1,7 @@
 /*
  * libkvstore -- KV-cache store for MI355X (gfx950).
  *
- * Two store operations and their error reporting, as a plain C ABI.  Every
+ * Three store operations and their error reporting, as a plain C ABI.  Every
  * pointer argument of a store call is a DEVICE pointer owned by the caller
  * (for example a torch tensor's data pointer); the library never allocates,
  * frees or synchronises inside a store call.  Work is enqueued on the given
@@ -22,6 +22,10 @@
  *                         offset = loc % page_size; every element x of K (V)
  *                         becomes e4m3fn(x * inv_k) (e4m3fn(x * inv_v)) at
  *                         [page, offset, head, dim] of the K (V) cache.
+ *   kvstore_fp8_paged_dynamic -- the same store with per-token (or per token
+ *                         and head) scales computed in the kernel, the step
+ *                         the docstring of "trtllm_fp8_kv_kernel.py" lists as
+ *                         "per-token or per-page scale computation".
  *
  * Numerics of kvstore_fp8_paged: x (bf16 or fp16) is widened to fp32 exactly,
  * multiplied once in fp32 (round to nearest) by the inverse scale, and
@@ -57,8 +61,11 @@ extern "C" {
 /* Index element types. */
 enum { KVSTORE_IDX_I32 = 0, KVSTORE_IDX_I64 = 1 };
 
-/* Source element types of kvstore_fp8_paged. */
+/* Source element types of kvstore_fp8_paged / kvstore_fp8_paged_dynamic. */
 enum { KVSTORE_SRC_BF16 = 0, KVSTORE_SRC_FP16 = 1 };
+
+/* Scale groups of kvstore_fp8_paged_dynamic. */
+enum { KVSTORE_SCALE_PER_TOKEN = 0, KVSTORE_SCALE_PER_TOKEN_HEAD = 1 };
 
 /* Status codes.  Negative codes returned by a store call mean nothing was
  * launched and no memory was touched. */
@@ -141,6 +148,45 @@ int kvstore_fp8_paged(const void* k, const void* v, void* k_cache, void* v_cache
                       int64_t vc_stride_head_bytes, uint32_t batch, int64_t size_limit,
                       int64_t page_size, const float* inv_k_scale_ptr,
                       const float* inv_v_scale_ptr, hipStream_t stream);
+
+/*
+ * Fused FP8 (e4m3fn) quantise + paged store with dynamic scales.  The
+ * docstring of sglang "trtllm_fp8_kv_kernel.py" lists per-token scale
+ * computation among the fused kernel's steps (its code only applies a given
+ * per-tensor scale); this call computes the scales itself.
+ *
+ * For each valid token and each of K and V, the scale groups are the whole
+ * row (granularity KVSTORE_SCALE_PER_TOKEN) or each head
+ * (KVSTORE_SCALE_PER_TOKEN_HEAD).  Per group: amax = max |x| (NaN elements
+ * ignored); scale = max(amax / 448, 2^-126) in fp32 (correctly rounded; the
+ * floor keeps 1/scale finite); inv = 1 / scale in fp32; every element becomes
+ * e4m3fn(x * inv) with the rules of kvstore_fp8_paged; and the fp32 scale of
+ * group g is written at byte offset page * *s_stride_page_bytes +
+ * off * *s_stride_offset_bytes + g * *s_stride_head_bytes of k_scale_cache /
+ * v_scale_cache (the head stride is unused per token).  Dequantisation is
+ * code value * scale.
+ *
+ *   All other arguments: as in kvstore_fp8_paged.
+ *   k_scale_cache, v_scale_cache  device fp32 arrays, 4-byte aligned; scale
+ *                strides >= 0 and multiples of 4.
+ * Limits: num_heads * head_dim <= 4096 (one 64-lane wave holds the whole
+ * row); per head additionally head_dim in {16, 32, 64, ..., 1024}.  Larger
+ * shapes return KVSTORE_ERR_SHAPE.  Unknown granularity: KVSTORE_ERR_DTYPE.
+ */
+int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void* v_cache,
+                              const void* indices, int idx_dtype, int64_t idx_stride,
+                              int src_dtype, int32_t num_heads, int32_t head_dim,
+                              int64_t k_stride_token_bytes, int64_t k_stride_head_bytes,
+                              int64_t v_stride_token_bytes, int64_t v_stride_head_bytes,
+                              int64_t kc_stride_page_bytes, int64_t kc_stride_offset_bytes,
+                              int64_t kc_stride_head_bytes, int64_t vc_stride_page_bytes,
+                              int64_t vc_stride_offset_bytes, int64_t vc_stride_head_bytes,
+                              float* k_scale_cache, float* v_scale_cache, int granularity,
+                              int64_t ks_stride_page_bytes, int64_t ks_stride_offset_bytes,
+                              int64_t ks_stride_head_bytes, int64_t vs_stride_page_bytes,
+                              int64_t vs_stride_offset_bytes, int64_t vs_stride_head_bytes,
+                              uint32_t batch, int64_t size_limit, int64_t page_size,
+                              hipStream_t stream);
 
 /*
  * Waits for `stream`, then reads and clears the current device's error flag.

@@ -39,7 +39,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["kvstore_copy", "kvstore_fp8_paged", "kvstore_check_error", "kvstore_strerror"])
+        ["kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_dynamic", "kvstore_check_error",
+         "kvstore_strerror"])
 
 
 def test_library_exports_every_declared_symbol(kv):
@@ -170,3 +171,55 @@ def test_valid_arguments_reach_the_runtime(kv):
     # With no GPU the launch itself fails: the call got past validation.
     assert _copy_call(kv) == kv.ERR_HIP
     assert _fp8_call(kv) == kv.ERR_HIP
+
+
+DYN_OK = dict(FP8_OK, k_scale_cache=A + 0x600000, v_scale_cache=A + 0x700000, granularity=1,
+              ks_stride_page_bytes=64 * 32, ks_stride_offset_bytes=32, ks_stride_head_bytes=4,
+              vs_stride_page_bytes=64 * 32, vs_stride_offset_bytes=32, vs_stride_head_bytes=4)
+
+DYN_BAD = [
+    ("null_scale_cache", dict(v_scale_cache=0), -1),
+    ("bad_granularity", dict(granularity=2), -4),
+    ("row_too_wide", dict(num_heads=40), -2),                 # 5120 elements > 4096
+    ("head_not_pow2_per_head", dict(num_heads=3, head_dim=48, k_stride_token_bytes=2048,
+                                    v_stride_token_bytes=2048, k_stride_head_bytes=96,
+                                    v_stride_head_bytes=96, kc_stride_head_bytes=48,
+                                    vc_stride_head_bytes=48), -2),
+    ("head_too_wide_per_head", dict(num_heads=2, head_dim=2048, k_stride_head_bytes=4096,
+                                    v_stride_head_bytes=4096, kc_stride_head_bytes=2048,
+                                    vc_stride_head_bytes=2048, k_stride_token_bytes=8192,
+                                    v_stride_token_bytes=8192), -2),
+    ("scale_misaligned", dict(k_scale_cache=A + 0x600002), -3),
+    ("scale_stride_misaligned", dict(vs_stride_offset_bytes=34), -3),
+    ("scale_stride_negative", dict(ks_stride_head_bytes=-4), -2),
+    ("scale_offset_overflow", dict(ks_stride_page_bytes=1 << 61, size_limit=1 << 20), -2),
+    ("inherits_fp8_checks", dict(head_dim=120), -2),
+]
+
+
+def _dyn_call(kv, **over):
+    a = dict(DYN_OK, **over)
+    return kv.kvstore_fp8_paged_dynamic(*[a[n] for n in (
+        "k", "v", "k_cache", "v_cache", "indices", "idx_dtype", "idx_stride", "src_dtype",
+        "num_heads", "head_dim", "k_stride_token_bytes", "k_stride_head_bytes",
+        "v_stride_token_bytes", "v_stride_head_bytes", "kc_stride_page_bytes",
+        "kc_stride_offset_bytes", "kc_stride_head_bytes", "vc_stride_page_bytes",
+        "vc_stride_offset_bytes", "vc_stride_head_bytes", "k_scale_cache", "v_scale_cache",
+        "granularity", "ks_stride_page_bytes", "ks_stride_offset_bytes", "ks_stride_head_bytes",
+        "vs_stride_page_bytes", "vs_stride_offset_bytes", "vs_stride_head_bytes", "batch",
+        "size_limit", "page_size")], None)
+
+
+@cpu_only
+@pytest.mark.parametrize("name,over,status", DYN_BAD, ids=[c[0] for c in DYN_BAD])
+def test_dynamic_rejects(kv, name, over, status):
+    assert _dyn_call(kv, **over) == status
+
+
+@cpu_only
+def test_dynamic_valid_arguments_reach_the_runtime(kv):
+    assert _dyn_call(kv) == kv.ERR_HIP
+    assert _dyn_call(kv, granularity=0, num_heads=3, head_dim=48, k_stride_token_bytes=2048,
+                     v_stride_token_bytes=2048, k_stride_head_bytes=96, v_stride_head_bytes=96,
+                     kc_stride_head_bytes=48, vc_stride_head_bytes=48) == kv.ERR_HIP
+    assert _dyn_call(kv, batch=0, k=0) == kv.OK
