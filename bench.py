@@ -210,6 +210,7 @@ def main():
     next_rows = None
     if not args.no_next:
         next_rows = bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh)
+        next_rows.update(bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh))
 
     traffic = stored_traffic()
     roofline = {
@@ -319,6 +320,45 @@ def bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh, n=50):
     assert st == kv.OK
     del kc, vc
     return out
+
+
+def bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh, n=100):
+    """Tensor-parallel share of the prefill copy: one 128-dim bf16 head per
+    GPU, i.e. 256-byte rows (packed four to a wave), same tokens and slots."""
+    dev = k3[0].device
+    R = 256
+    ks = [k3[s][:, :128].contiguous() for s in range(S)]
+    vs = [v3[s][:, :128].contiguous() for s in range(S)]
+    kc = torch.full((c3.slots, R), 0xFF, dtype=torch.uint8, device=dev)
+    vc = torch.full_like(kc, 0xFF)
+
+    def call(s):
+        st = kv.kvstore_copy(ks[s].data_ptr(), vs[s].data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                             i3[s].data_ptr(), kv.IDX_I32, 1, R, R, R, R, c3.num_tokens, c3.slots,
+                             sh)
+        if st:
+            raise kv.KVStoreError(st, "kvstore_copy")
+
+    for i in range(5):
+        call(i % S)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(torch.cuda.current_stream())
+    for i in range(n):
+        call(i % S)
+    e1.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    T = c3.num_tokens
+    b = 2 * T * R * 2 + T * 4
+    st, _, _ = kv.kvstore_check_error(sh)
+    assert st == kv.OK
+    del kc, vc, ks, vs
+    return {"copy_tp_share_256B_rows": {
+        "workload": "prefill copy with one 128-dim bf16 head per GPU (32768 tok, 256 B rows, "
+                    "int32, 2^21 slots in 16-slot pages)",
+        "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+        "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
 
 
 def bench_decode(kv, torch, dev, kvgen, to_dev):

@@ -11,7 +11,9 @@
 // Both are pure data movement, bound by HBM bandwidth; no MFMA and no LDS.
 // Design points for CDNA4:
 //   * one 64-lane wave per (token, slice of the row); each lane moves 16 B per
-//     access (dwordx4), so one wave access covers 1 KiB of a row;
+//     access (dwordx4), so one wave access covers 1 KiB of a row; rows or
+//     pointers aligned only to 8 or 4 bytes use 8- or 4-byte lanes, and rows
+//     that need at most 32 lanes are packed several to a wave;
 //   * every load of a wave (K and V, all its 1 KiB chunks) is issued before the
 //     index is needed: the source address does not depend on the index, so the
 //     index fetch overlaps the data fetch instead of preceding it;
@@ -67,6 +69,26 @@ __device__ __forceinline__ int64_t load_index(const void* indices, int64_t pos) 
   return (int64_t)static_cast<const IdxT*>(indices)[pos];
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Vector of VW bytes moved by one lane in one access (16, 8 or 4).
+template <int VW> struct LaneVec;
+template <> struct LaneVec<16> { typedef u32x4 type; };
+template <> struct LaneVec<8> { typedef u32x2 type; };
+template <> struct LaneVec<4> { typedef uint32_t type; };
+
+template <int VW>
+__device__ __forceinline__ typename LaneVec<VW>::type loadv(const uint8_t* base, uint32_t off) {
+  typedef typename LaneVec<VW>::type T;
+  return __builtin_nontemporal_load(reinterpret_cast<const T*>(base + off));
+}
+
+template <int VW>
+__device__ __forceinline__ void storev(uint8_t* base, uint32_t off, typename LaneVec<VW>::type v) {
+  typedef typename LaneVec<VW>::type T;
+  __builtin_nontemporal_store(v, reinterpret_cast<T*>(base + off));
+}
+
 __device__ __forceinline__ u32x4 load16(const uint8_t* base, uint32_t off) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
 }
@@ -103,10 +125,13 @@ struct CopyParams {
   uint32_t batch;
 };
 
-// Grid: x = ceil(batch / kCopyWavesPerBlock) blocks of kCopyWavesPerBlock
-// waves, one wave per token; y = slices of the row, kChunks 1 KiB chunks each.
-template <int kChunks, typename IdxT>
+// One row per wave.  Grid: x = ceil(batch / kCopyWavesPerBlock) blocks of
+// kCopyWavesPerBlock waves, one wave per token; y = slices of the row, kChunks
+// chunks of 64 * VW bytes each.
+template <int VW, int kChunks, typename IdxT>
 __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const CopyParams p) {
+  typedef typename LaneVec<VW>::type T;
+  constexpr uint32_t kChunk = kWave * VW;
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t token = wave_uniform(blockIdx.x * kCopyWavesPerBlock + threadIdx.x / kWave);
   if (token >= p.batch) return;
@@ -116,15 +141,15 @@ __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const C
 
   const uint8_t* ks = p.k + (int64_t)token * p.k_stride;
   const uint8_t* vs = p.v + (int64_t)token * p.v_stride;
-  const uint32_t col0 = slice * (kChunks * kChunkBytes) + lane * kLaneBytes;
+  const uint32_t col0 = slice * (kChunks * kChunk) + lane * VW;
 
-  u32x4 kr[kChunks], vr[kChunks];
+  T kr[kChunks], vr[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const uint32_t col = col0 + c * kChunkBytes;
+    const uint32_t col = col0 + c * kChunk;
     if (col < p.row_bytes) {
-      kr[c] = load16(ks, col);
-      vr[c] = load16(vs, col);
+      kr[c] = loadv<VW>(ks, col);
+      vr[c] = loadv<VW>(vs, col);
     }
   }
 
@@ -136,10 +161,55 @@ __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const C
   uint8_t* vd = p.v_cache + loc * p.cache_stride;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
-    const uint32_t col = col0 + c * kChunkBytes;
+    const uint32_t col = col0 + c * kChunk;
     if (col < p.row_bytes) {
-      store16(kd, col, kr[c]);
-      store16(vd, col, vr[c]);
+      storev<VW>(kd, col, kr[c]);
+      storev<VW>(vd, col, vr[c]);
+    }
+  }
+}
+
+// Several rows per wave, for rows that need at most 32 lanes.  Each aligned
+// group of 2^group_shift lanes owns kPackRows tokens (indices are per-lane
+// loads); lane c of a group moves bytes [c * VW, c * VW + VW) of each row.
+// All loads of a wave are issued before its stores.  Blocks of
+// kPackWavesPerBlock waves; grid x = ceil(batch / tokens per block).
+constexpr int kPackWavesPerBlock = 4;
+constexpr int kPackRows = 2;
+
+template <int VW, typename IdxT>
+__global__ __launch_bounds__(kWave * kPackWavesPerBlock) void kvstore_copy_packed_kernel(
+    const CopyParams p, uint32_t group_shift) {
+  typedef typename LaneVec<VW>::type T;
+  const uint32_t lane = threadIdx.x % kWave;
+  const uint32_t wave = blockIdx.x * kPackWavesPerBlock + threadIdx.x / kWave;
+  const uint32_t rows_per_wave = kWave >> group_shift;
+  const uint32_t col = (lane & ((1u << group_shift) - 1)) * VW;
+  const bool active = col < p.row_bytes;
+  T kr[kPackRows], vr[kPackRows];
+  int64_t loc[kPackRows];
+#pragma unroll
+  for (int r = 0; r < kPackRows; ++r) {
+    const uint64_t t = ((uint64_t)wave * kPackRows + r) * rows_per_wave + (lane >> group_shift);
+    if (t < p.batch) {
+      loc[r] = load_index<IdxT>(p.indices, (int64_t)t * p.idx_stride);
+      if (active) {
+        kr[r] = loadv<VW>(p.k + (int64_t)t * p.k_stride, col);
+        vr[r] = loadv<VW>(p.v + (int64_t)t * p.v_stride, col);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kPackRows; ++r) {
+    const uint64_t t = ((uint64_t)wave * kPackRows + r) * rows_per_wave + (lane >> group_shift);
+    if (t >= p.batch) continue;
+    if (loc[r] < 0 || loc[r] >= p.size_limit) {
+      if (col == 0) report_bad_token((uint32_t)t);
+      continue;
+    }
+    if (active) {
+      storev<VW>(p.k_cache + loc[r] * p.cache_stride, col, kr[r]);
+      storev<VW>(p.v_cache + loc[r] * p.cache_stride, col, vr[r]);
     }
   }
 }
@@ -547,24 +617,44 @@ int64_t lds_per_cu() {
   return cache[dev];
 }
 
-template <typename IdxT>
-int launch_copy(const CopyParams& p, hipStream_t stream) {
-  const int64_t chunks = ceil_div(p.row_bytes, kChunkBytes);
+template <int VW, typename IdxT>
+int launch_copy_vw(const CopyParams& p, hipStream_t stream) {
+  constexpr int64_t kChunk = kWave * VW;
+  const dim3 block(kCopyBlockThreads);
+  const int64_t lanes = ceil_div(p.row_bytes, VW);
+  if (lanes <= kWave / 2) {
+    // several rows per wave: groups of the next power of two >= lanes
+    uint32_t shift = 0;
+    while ((int64_t(1) << shift) < lanes) ++shift;
+    const int64_t rows_per_block = (int64_t)kPackWavesPerBlock * kPackRows * (kWave >> shift);
+    const dim3 grid((uint32_t)ceil_div(p.batch, rows_per_block));
+    hipLaunchKernelGGL((kvstore_copy_packed_kernel<VW, IdxT>), grid,
+                       dim3(kWave * kPackWavesPerBlock), 0, stream, p, shift);
+    return launch_status();
+  }
+  const int64_t chunks = ceil_div(p.row_bytes, kChunk);
   const int per_wave = (int)(chunks < kMaxChunksPerWave ? chunks : kMaxChunksPerWave);
   const int64_t slices = ceil_div(chunks, per_wave);
   if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
   const dim3 grid((uint32_t)ceil_div(p.batch, kCopyWavesPerBlock), (uint32_t)slices);
-  const dim3 block(kCopyBlockThreads);
-  // The kernel uses no LDS; the dynamic allocation only caps residency.
-  const int64_t lds = lds_per_cu();
+  // The kernel uses no LDS; the dynamic allocation only caps residency (tuned
+  // for 16-byte lanes, where a wave has the most bytes in flight).
+  const int64_t lds = VW == 16 ? lds_per_cu() : 0;
   const uint32_t lds_bytes = lds > 0 ? (uint32_t)(lds / copy_blocks_per_cu(per_wave)) : 0;
   switch (per_wave) {
-    case 1: hipLaunchKernelGGL((kvstore_copy_kernel<1, IdxT>), grid, block, lds_bytes, stream, p); break;
-    case 2: hipLaunchKernelGGL((kvstore_copy_kernel<2, IdxT>), grid, block, lds_bytes, stream, p); break;
-    case 3: hipLaunchKernelGGL((kvstore_copy_kernel<3, IdxT>), grid, block, lds_bytes, stream, p); break;
-    default: hipLaunchKernelGGL((kvstore_copy_kernel<4, IdxT>), grid, block, lds_bytes, stream, p); break;
+    case 1: hipLaunchKernelGGL((kvstore_copy_kernel<VW, 1, IdxT>), grid, block, lds_bytes, stream, p); break;
+    case 2: hipLaunchKernelGGL((kvstore_copy_kernel<VW, 2, IdxT>), grid, block, lds_bytes, stream, p); break;
+    case 3: hipLaunchKernelGGL((kvstore_copy_kernel<VW, 3, IdxT>), grid, block, lds_bytes, stream, p); break;
+    default: hipLaunchKernelGGL((kvstore_copy_kernel<VW, 4, IdxT>), grid, block, lds_bytes, stream, p); break;
   }
   return launch_status();
+}
+
+template <typename IdxT>
+int launch_copy(const CopyParams& p, int vw, hipStream_t stream) {
+  if (vw == 16) return launch_copy_vw<16, IdxT>(p, stream);
+  if (vw == 8) return launch_copy_vw<8, IdxT>(p, stream);
+  return launch_copy_vw<4, IdxT>(p, stream);
 }
 
 template <int kPasses, bool kFlat, bool kFp16>
@@ -725,17 +815,20 @@ int kvstore_copy(const void* k, const void* v, void* k_cache, void* v_cache,
   if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
   if (batch == 0) return KVSTORE_OK;
   if (!k || !v || !k_cache || !v_cache || !indices) return KVSTORE_ERR_NULL;
-  if (row_bytes <= 0 || row_bytes > INT32_MAX || row_bytes % kLaneBytes) return KVSTORE_ERR_SHAPE;
+  if (row_bytes <= 0 || row_bytes > INT32_MAX || row_bytes % 4) return KVSTORE_ERR_SHAPE;
   if (k_stride_bytes < 0 || v_stride_bytes < 0 || cache_stride_bytes < row_bytes)
     return KVSTORE_ERR_SHAPE;
   if (size_limit <= 0 || !fits(size_limit, cache_stride_bytes)) return KVSTORE_ERR_SHAPE;
   if (!fits(batch, k_stride_bytes) || !fits(batch, v_stride_bytes)) return KVSTORE_ERR_SHAPE;
   const int ic = check_index_args(indices, idx_dtype, idx_stride, batch);
   if (ic != KVSTORE_OK) return ic;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
-      !aligned(k_stride_bytes, 16) || !aligned(v_stride_bytes, 16) ||
-      !aligned(cache_stride_bytes, 16))
-    return KVSTORE_ERR_ALIGN;
+  // Widest lane vector (16, 8 or 4 bytes) that every row start and the row
+  // size allow.
+  const uintptr_t bits = (uintptr_t)k | (uintptr_t)v | (uintptr_t)k_cache | (uintptr_t)v_cache |
+                         (uintptr_t)k_stride_bytes | (uintptr_t)v_stride_bytes |
+                         (uintptr_t)cache_stride_bytes | (uintptr_t)row_bytes;
+  const int vw = (bits % 16 == 0) ? 16 : (bits % 8 == 0) ? 8 : (bits % 4 == 0) ? 4 : 0;
+  if (vw == 0) return KVSTORE_ERR_ALIGN;
 
   CopyParams p;
   p.k = static_cast<const uint8_t*>(k);
@@ -750,8 +843,8 @@ int kvstore_copy(const void* k, const void* v, void* k_cache, void* v_cache,
   p.size_limit = size_limit;
   p.row_bytes = (uint32_t)row_bytes;
   p.batch = batch;
-  return idx_dtype == KVSTORE_IDX_I64 ? launch_copy<int64_t>(p, stream)
-                                      : launch_copy<int32_t>(p, stream);
+  return idx_dtype == KVSTORE_IDX_I64 ? launch_copy<int64_t>(p, vw, stream)
+                                      : launch_copy<int32_t>(p, vw, stream);
 }
 
 int kvstore_fp8_paged(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -90,16 +90,20 @@ enum {
  *   indices      device, element t at indices[t * idx_stride], of type
  *                idx_dtype (KVSTORE_IDX_I32 / KVSTORE_IDX_I64).
  *   idx_stride   in elements, >= 1.
- *   row_bytes    bytes per K (and V) row: > 0, a multiple of 16, < 2^31.
- *   *_stride_bytes  multiples of 16; k/v strides >= 0,
+ *   row_bytes    bytes per K (and V) row: > 0, a multiple of 4, < 2^31.
+ *   *_stride_bytes  multiples of 4; k/v strides >= 0,
  *                cache_stride_bytes >= row_bytes.
  *   batch        number of tokens; 0 returns KVSTORE_OK and launches nothing.
  *   size_limit   valid slots are [0, size_limit); > 0, and
  *                size_limit * cache_stride_bytes must fit in int64.
  *   stream       HIP stream of the current device (0 = null stream).
  *
- * Alignment: k, v, k_cache, v_cache 16-byte aligned; indices aligned to its
- * element size.  Element data is never interpreted, so any element type works.
+ * Alignment: k, v, k_cache, v_cache 4-byte aligned; indices aligned to its
+ * element size.  Lanes move 16 bytes when the row size, the four pointers and
+ * the three strides are all multiples of 16 (the fast path), else 8 or 4
+ * bytes, as the page's kernel picks its vector width from the row size.  Rows
+ * of at most 32 lane vectors are packed several to a 64-lane wave.
+ * Element data is never interpreted, so any element type works.
  * Returns KVSTORE_OK or a negative status (nothing launched).
  */
 int kvstore_copy(const void* k, const void* v, void* k_cache, void* v_cache,

@@ -78,7 +78,7 @@ COPY_BAD = [
     ("bad_idx_dtype", dict(idx_dtype=2), -4),
     ("row_zero", dict(row_bytes=0), -2),
     ("row_negative", dict(row_bytes=-16), -2),
-    ("row_not_16", dict(row_bytes=2040, k_stride_bytes=2048, cache_stride_bytes=2048), -2),
+    ("row_not_4", dict(row_bytes=2042, k_stride_bytes=2048, cache_stride_bytes=2048), -2),
     ("row_too_big", dict(row_bytes=1 << 31, cache_stride_bytes=1 << 31, k_stride_bytes=0,
                          v_stride_bytes=0), -2),
     ("cache_stride_below_row", dict(cache_stride_bytes=1024), -2),
@@ -87,10 +87,10 @@ COPY_BAD = [
     ("size_limit_overflow", dict(size_limit=1 << 62), -2),
     ("idx_stride_zero", dict(idx_stride=0), -2),
     ("idx_stride_huge", dict(idx_stride=1 << 62), -2),
-    ("k_misaligned", dict(k=A + 8), -3),
-    ("cache_misaligned", dict(k_cache=A + 4), -3),
-    ("stride_misaligned", dict(k_stride_bytes=2056), -3),
-    ("cache_stride_misaligned", dict(cache_stride_bytes=2056), -3),
+    ("k_misaligned", dict(k=A + 2), -3),
+    ("cache_misaligned", dict(k_cache=A + 1), -3),
+    ("stride_misaligned", dict(k_stride_bytes=2050), -3),
+    ("cache_stride_misaligned", dict(cache_stride_bytes=2054), -3),
     ("i32_index_misaligned", dict(indices=A + 2), -3),
     ("i64_index_misaligned", dict(indices=A + 4, idx_dtype=1), -3),
 ]
@@ -171,6 +171,10 @@ def test_valid_arguments_reach_the_runtime(kv):
     # With no GPU the launch itself fails: the call got past validation.
     assert _copy_call(kv) == kv.ERR_HIP
     assert _fp8_call(kv) == kv.ERR_HIP
+    # 8- and 4-byte aligned rows and pointers are accepted by the copy
+    assert _copy_call(kv, row_bytes=2040, k=A + 8) == kv.ERR_HIP
+    assert _copy_call(kv, row_bytes=36, k_stride_bytes=36, v_stride_bytes=40,
+                      cache_stride_bytes=36, v_cache=A + 0x300004) == kv.ERR_HIP
 
 
 DYN_OK = dict(FP8_OK, k_scale_cache=A + 0x600000, v_scale_cache=A + 0x700000, granularity=1,

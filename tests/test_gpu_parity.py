@@ -448,3 +448,77 @@ def test_graph_capture_replays_match_eager():
         assert_cache_equal(kc4, okc4, f"replay {replay} k_cache (fp8)")
         assert_cache_equal(vc4, ovc4, f"replay {replay} v_cache (fp8)")
     assert check_flag() == (kv.OK, -1, 0)
+
+
+# ---------------------------------------------------------------------------
+# Narrow alignment (8- and 4-byte lanes) and packed small rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("row,stride,ptr_off,idx64", [
+    (4, 4, 0, False), (12, 20, 4, True), (36, 44, 4, False), (100, 104, 8, False),
+    (128, 136, 8, True), (132, 132, 4, False), (252, 260, 4, False), (256, 256, 8, False),
+    (504, 512, 8, False), (1020, 1028, 4, True), (2052, 2060, 4, False), (4104, 4112, 8, False),
+    (16, 16, 0, False), (48, 64, 0, True), (256, 256, 0, False), (512, 528, 0, False)])
+def test_copy_narrow_and_packed_rows(row, stride, ptr_off, idx64):
+    rng = np.random.Generator(np.random.PCG64(row * 31 + ptr_off))
+    T, slots = 301, 800
+    kb = rng.integers(0, 256, (T, stride), dtype=np.uint8)
+    vb = rng.integers(0, 256, (T, stride), dtype=np.uint8)
+    idx = rng.permutation(slots)[:T].astype(np.int64 if idx64 else np.int32)
+    _say(f"narrow row={row} stride={stride} off={ptr_off}")
+    # device buffers with the data placed ptr_off bytes past a 256-byte boundary
+    kd = torch.zeros(T * stride + 64, dtype=torch.uint8, device=DEV)
+    vd = torch.zeros_like(kd)
+    kd[ptr_off:ptr_off + T * stride] = torch.from_numpy(kb.reshape(-1)).to(DEV)
+    vd[ptr_off:ptr_off + T * stride] = torch.from_numpy(vb.reshape(-1)).to(DEV)
+    kc = torch.full((slots * row + 64,), 0xFF, dtype=torch.uint8, device=DEV)
+    vc = torch.full_like(kc, 0xFF)
+    di = to_dev(idx)
+    st = kv.kvstore_copy(kd.data_ptr() + ptr_off, vd.data_ptr() + ptr_off,
+                         kc.data_ptr() + ptr_off, vc.data_ptr() + ptr_off, di.data_ptr(),
+                         kv.IDX_I64 if idx64 else kv.IDX_I32, 1, row, stride, stride, row, T,
+                         slots, torch.cuda.current_stream().cuda_stream)
+    assert st == kv.OK
+    assert check_flag() == (kv.OK, -1, 0)
+    okc = np.full(slots * row + 64, 0xFF, dtype=np.uint8)
+    ovc = np.full_like(okc, 0xFF)
+    ost = oracle.copy(kb, vb, okc[ptr_off:], ovc[ptr_off:], idx, row_bytes=row, k_stride=stride,
+                      v_stride=stride, cache_stride=row, size_limit=slots)
+    assert ost == (T, -1, 0)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
+def test_copy_packed_rows_out_of_range():
+    # 256-byte rows pack four tokens to a wave; bad tokens in one wave must not
+    # disturb their neighbours.
+    rng = np.random.Generator(np.random.PCG64(77))
+    T, slots, row = 64, 256, 256
+    kb = rng.integers(0, 256, (T, row), dtype=np.uint8)
+    vb = rng.integers(0, 256, (T, row), dtype=np.uint8)
+    idx = rng.permutation(200)[:T].astype(np.int32)
+    idx[1], idx[2], idx[40] = -1, 200, 10 ** 9
+    c = kvgen.Case(name="packed_oob", kind="copy", src_dtype="bf16", num_tokens=T, num_heads=1,
+                   head_dim=row // 2, in_stride_elems=row // 2, k=kb.view(np.uint16),
+                   v=vb.view(np.uint16), indices=idx, idx_dtype="i32", slots=slots)
+    kc = sentinel_cache(slots, row)
+    vc = sentinel_cache(slots, row)
+    assert run_copy(c, kc, vc, size_limit=200) == kv.OK
+    assert check_flag() == (kv.ERR_OOB, 1, 3)
+    okc = np.full((slots, row), 0xFF, dtype=np.uint8)
+    ovc = np.full_like(okc, 0xFF)
+    assert oracle.copy(kb, vb, okc, ovc, idx, row_bytes=row, k_stride=row, v_stride=row,
+                       cache_stride=row, size_limit=200) == (T - 3, 1, 3)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
+def test_copy_tensor_parallel_share_full_size():
+    # One 128-dim bf16 head per GPU (8 KV heads over 8 GPUs): the prefill
+    # workload's tokens and page pattern with 256-byte rows.
+    c = kvgen.workload(3)
+    rows = kvgen.workload(3).k[:, :128].copy()
+    c.k = rows
+    c.v = kvgen.workload(3).v[:, 128:256].copy()
+    c.num_heads, c.head_dim, c.in_stride_elems = 1, 128, 128
+    copy_parity(c)

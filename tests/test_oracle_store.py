@@ -54,6 +54,26 @@ def test_copy_matches_python_bruteforce(n, tokens, slots):
     np.testing.assert_array_equal(vc, bv)
 
 
+@pytest.mark.parametrize("row,stride", [(4, 4), (12, 20), (36, 44), (8, 8), (24, 40), (100, 104)])
+def test_copy_rows_of_four_byte_multiples_match_bruteforce(row, stride):
+    # The copy page accepts any row size that is a multiple of 4 bytes
+    # (kvcache.cuh, copy_kv_warp: vectors of 16, 8 or 4 bytes).
+    rng = np.random.Generator(np.random.PCG64(row))
+    T, slots = 37, 64
+    kb = rng.integers(0, 256, (T, stride), dtype=np.uint8)
+    vb = rng.integers(0, 256, (T, stride), dtype=np.uint8)
+    idx = rng.permutation(slots)[:T].astype(np.int32)
+    kc = np.full((slots, row), 0xFF, dtype=np.uint8)
+    vc = np.full_like(kc, 0xFF)
+    st = oracle.copy(kb, vb, kc, vc, idx, row_bytes=row, k_stride=stride, v_stride=stride,
+                     cache_stride=row, size_limit=slots)
+    bk, bv, bad = _ref.copy_bruteforce(kb.tobytes(), vb.tobytes(), idx, row, stride, stride,
+                                       slots, row, slots)
+    assert st == (T, -1, 0) and bad == []
+    np.testing.assert_array_equal(kc, bk)
+    np.testing.assert_array_equal(vc, bv)
+
+
 @pytest.mark.parametrize("n,tokens,slots", [(2, 300, 4096), (3, 1000, 4096), (5, 257, 2048)])
 def test_copy_roundtrip_and_sentinel(n, tokens, slots):
     c = small_copy_case(n, tokens, slots)
