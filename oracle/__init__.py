@@ -64,6 +64,14 @@ def _bind(lib):
                                      i64, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                      i64, i64, i64, vp, vp, vp, vp]
     lib.oracle_fp8_paged.restype = i64
+    lib.oracle_e5m2_from_float.argtypes = [C.c_float]
+    lib.oracle_e5m2_from_float.restype = C.c_uint8
+    lib.oracle_e5m2_array.argtypes = [vp, i64, vp]
+    lib.oracle_e5m2_array.restype = None
+    lib.oracle_quantize_e5m2.argtypes = [vp, i64, i32, vp, vp]
+    lib.oracle_quantize_e5m2.restype = None
+    lib.oracle_fp8_paged_e5m2.argtypes = lib.oracle_fp8_paged.argtypes
+    lib.oracle_fp8_paged_e5m2.restype = i64
     lib.oracle_fp8_paged_dynamic.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, i64, i64,
                                              i64, i64, i64, i64, i64, i64, i64, i64, i64, i64,
                                              vp, vp, i64, i64, i64, i64, i64, i64, i32,
@@ -95,14 +103,25 @@ def e4m3fn(y: np.ndarray, lib=None) -> np.ndarray:
     return out
 
 
-def quantize(bits: np.ndarray, src_dtype: str, inv_bits: Optional[int], lib=None) -> np.ndarray:
-    """e4m3fn(decode(bits) * inv) for each 16-bit input pattern."""
+def e5m2(y: np.ndarray, lib=None) -> np.ndarray:
+    """Saturating round-to-nearest-even e5m2 codes of fp32 values."""
+    lib = lib or load()
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    lib.oracle_e5m2_array(_ptr(y), y.size, _ptr(out))
+    return out
+
+
+def quantize(bits: np.ndarray, src_dtype: str, inv_bits: Optional[int], lib=None,
+             fmt: str = "e4m3fn") -> np.ndarray:
+    """fmt(decode(bits) * inv) for each 16-bit input pattern (fmt e4m3fn or e5m2)."""
     lib = lib or load()
     bits = np.ascontiguousarray(bits, dtype=np.uint16)
     out = np.empty(bits.shape, dtype=np.uint8)
     inv = _f32_box(inv_bits)
-    lib.oracle_quantize(_ptr(bits), bits.size, int(src_dtype == "fp16"),
-                        None if inv is None else _ptr(inv), _ptr(out))
+    fn = lib.oracle_quantize_e5m2 if fmt == "e5m2" else lib.oracle_quantize
+    fn(_ptr(bits), bits.size, int(src_dtype == "fp16"), None if inv is None else _ptr(inv),
+       _ptr(out))
     return out
 
 
@@ -140,10 +159,10 @@ def fp8_paged(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.nda
               indices: np.ndarray, *, src_dtype: str, num_heads: int, head_dim: int,
               k_strides, v_strides, kc_strides, vc_strides, size_limit: int, page_size: int,
               inv_k_bits: Optional[int], inv_v_bits: Optional[int],
-              batch: Optional[int] = None, idx_stride: int = 1, lib=None):
-    """Fused FP8 paged store.  k_strides/v_strides = (token, head) in bytes;
-    kc_strides/vc_strides = (page, offset, head) in bytes.
-    Returns (rows_written, first_bad_token, bad_count)."""
+              batch: Optional[int] = None, idx_stride: int = 1, lib=None, fmt: str = "e4m3fn"):
+    """Fused FP8 paged store (e4m3fn or e5m2 caches).  k_strides/v_strides =
+    (token, head) in bytes; kc_strides/vc_strides = (page, offset, head) in
+    bytes.  Returns (rows_written, first_bad_token, bad_count)."""
     lib = lib or load()
     fb = np.zeros(1, dtype=np.int64)
     bc = np.zeros(1, dtype=np.uint64)
@@ -152,7 +171,8 @@ def fp8_paged(k: np.ndarray, v: np.ndarray, k_cache: np.ndarray, v_cache: np.nda
     is64 = int(indices.dtype == np.int64)
     if batch is None:
         batch = (indices.size + idx_stride - 1) // idx_stride
-    n = lib.oracle_fp8_paged(
+    fn = lib.oracle_fp8_paged_e5m2 if fmt == "e5m2" else lib.oracle_fp8_paged
+    n = fn(
         _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(indices), is64, idx_stride,
         int(src_dtype == "fp16"), num_heads, head_dim, k_strides[0], k_strides[1],
         v_strides[0], v_strides[1], kc_strides[0], kc_strides[1], kc_strides[2],
@@ -213,7 +233,7 @@ def run_case_dynamic(case, per_head: bool, lib=None):
 # --------------------------------------------------------------------------
 
 def run_case(case, k_cache: Optional[np.ndarray] = None, v_cache: Optional[np.ndarray] = None,
-             indices: Optional[np.ndarray] = None, lib=None):
+             indices: Optional[np.ndarray] = None, lib=None, fmt: str = "e4m3fn"):
     """Run the oracle on a kvgen.Case with contiguous sentinel-filled caches
     (``[slots, cache_row_bytes]`` uint8) unless caches are given.
     Returns (k_cache, v_cache, (rows_written, first_bad, bad_count))."""
@@ -234,5 +254,5 @@ def run_case(case, k_cache: Optional[np.ndarray] = None, v_cache: Optional[np.nd
                        num_heads=H, head_dim=D, k_strides=(case.in_stride_bytes, 2 * D),
                        v_strides=(case.in_stride_bytes, 2 * D), kc_strides=cs, vc_strides=cs,
                        size_limit=case.slots, page_size=P, inv_k_bits=case.inv_k_bits,
-                       inv_v_bits=case.inv_v_bits, lib=lib)
+                       inv_v_bits=case.inv_v_bits, lib=lib, fmt=fmt)
     return k_cache, v_cache, st

@@ -29,6 +29,12 @@
  *     taken is round-to-nearest-even with saturation to +-448 (a NaN stays a
  *     NaN and keeps its sign).
  *
+ *   - e5m2 caches: the page's unfused path stores into float8_e5m2 as well as
+ *     float8_e4m3fn caches (its uint8-view condition names both).  The e5m2
+ *     encoding is written from its definition: 1 sign bit, 5 exponent bits
+ *     with bias 15, 2 mantissa bits, exponent 31 = infinity (mantissa 0) or
+ *     NaN, largest finite 57344.  Same reading as for e4m3fn: round to nearest
+ *     even, saturate to +-57344 (infinities too), NaN -> 0x7F | sign.
  *   - Dynamic scales (the docstring of "trtllm_fp8_kv_kernel.py" lists
  *     per-token scale computation among the fused kernel's steps; its code
  *     only takes a given per-tensor scale).  Reading taken: per group (a
@@ -147,10 +153,40 @@ uint8_t oracle_e4m3fn_from_float(float y) {
     return (uint8_t)((((e + 7) << 3) | ((int)m - 8)) | s);
 }
 
+uint8_t oracle_e5m2_from_float(float y) {
+    uint8_t s = signbit(y) ? 0x80 : 0x00;
+    if (isnan(y)) return (uint8_t)(0x7F | s);
+    double a = fabs((double)y);
+    if (a > 57344.0) return (uint8_t)(0x7B | s); /* includes +-inf */
+    if (a < ldexp(1.0, -14)) {
+        /* subnormal range: value = m * 2^-16, m in 0..3; m == 4 is the
+           smallest normal 2^-14, whose code 0x04 continues the sequence. */
+        double m = round_half_even(a * 65536.0); /* exact scaling by 2^16 */
+        return (uint8_t)((uint8_t)m | s);
+    }
+    int ex;
+    frexp(a, &ex);                               /* a = f * 2^ex, f in [0.5, 1) */
+    int e = ex - 1;                              /* floor(log2 a), >= -14 */
+    double m = round_half_even(ldexp(a, 2 - e)); /* a / 2^(e-2), in [4, 8] */
+    if (m == 8.0) {                              /* rounding carried into the exponent */
+        e += 1;
+        m = 4.0;
+    }
+    return (uint8_t)((((e + 15) << 2) | ((int)m - 4)) | s);
+}
+
+/* FP8 storage formats of the fused stores. */
+enum { FMT_E4M3FN = 0, FMT_E5M2 = 1 };
+
 /* One element of the fused store: decode, scale, encode. */
-static uint8_t quantize_one(uint16_t bits, int src_is_fp16, float inv) {
+static uint8_t quantize_fmt(uint16_t bits, int src_is_fp16, float inv, int fmt) {
     float x = src_to_float(bits, src_is_fp16);
-    return oracle_e4m3fn_from_float(mul_f32(x, inv));
+    float y = mul_f32(x, inv);
+    return fmt == FMT_E5M2 ? oracle_e5m2_from_float(y) : oracle_e4m3fn_from_float(y);
+}
+
+static uint8_t quantize_one(uint16_t bits, int src_is_fp16, float inv) {
+    return quantize_fmt(bits, src_is_fp16, inv, FMT_E4M3FN);
 }
 
 /* ---------------------------------------------------------------------- */
@@ -172,6 +208,17 @@ void oracle_quantize(const uint16_t* src, int64_t n, int src_is_fp16, const floa
 
 void oracle_e4m3fn_array(const float* y, int64_t n, uint8_t* out) {
     for (int64_t i = 0; i < n; ++i) out[i] = oracle_e4m3fn_from_float(y[i]);
+}
+
+void oracle_e5m2_array(const float* y, int64_t n, uint8_t* out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_e5m2_from_float(y[i]);
+}
+
+/* out[i] = e5m2(src[i] * inv); inv == NULL means 1.0. */
+void oracle_quantize_e5m2(const uint16_t* src, int64_t n, int src_is_fp16, const float* inv,
+                          uint8_t* out) {
+    float s = inv ? *inv : 1.0f;
+    for (int64_t i = 0; i < n; ++i) out[i] = quantize_fmt(src[i], src_is_fp16, s, FMT_E5M2);
 }
 
 /* ---------------------------------------------------------------------- */
@@ -219,13 +266,13 @@ int64_t oracle_copy(const uint8_t* k, const uint8_t* v, uint8_t* k_cache, uint8_
 static void store_fp8_row(const uint8_t* src, int64_t s_tok, int64_t s_head, int64_t t,
                           uint8_t* cache, int64_t s_page, int64_t s_off, int64_t s_chead,
                           int64_t page, int64_t off, int64_t num_heads, int64_t head_dim,
-                          int src_is_fp16, float inv) {
+                          int src_is_fp16, float inv, int fmt) {
     for (int64_t h = 0; h < num_heads; ++h) {
         for (int64_t d = 0; d < head_dim; ++d) {
             uint16_t bits;
             memcpy(&bits, src + t * s_tok + h * s_head + 2 * d, sizeof bits);
             cache[page * s_page + off * s_off + h * s_chead + d] =
-                quantize_one(bits, src_is_fp16, inv);
+                quantize_fmt(bits, src_is_fp16, inv, fmt);
         }
     }
 }
@@ -235,16 +282,17 @@ static void store_fp8_row(const uint8_t* src, int64_t s_tok, int64_t s_head, int
  * cache strides in bytes (dim stride is one byte).  inv_k / inv_v are host
  * pointers to fp32 inverse scales, NULL meaning 1.0.  Returns rows written.
  */
-int64_t oracle_fp8_paged(const uint8_t* k, const uint8_t* v, uint8_t* k_cache,
-                         uint8_t* v_cache, const void* indices, int idx_is_i64,
-                         int64_t idx_stride, int src_is_fp16, int64_t num_heads,
-                         int64_t head_dim, int64_t k_stride_token, int64_t k_stride_head,
-                         int64_t v_stride_token, int64_t v_stride_head,
-                         int64_t kc_stride_page, int64_t kc_stride_offset,
-                         int64_t kc_stride_head, int64_t vc_stride_page,
-                         int64_t vc_stride_offset, int64_t vc_stride_head, int64_t batch,
-                         int64_t size_limit, int64_t page_size, const float* inv_k,
-                         const float* inv_v, int64_t* first_bad, uint64_t* bad_count) {
+static int64_t fp8_paged_fmt(const uint8_t* k, const uint8_t* v, uint8_t* k_cache,
+                             uint8_t* v_cache, const void* indices, int idx_is_i64,
+                             int64_t idx_stride, int src_is_fp16, int64_t num_heads,
+                             int64_t head_dim, int64_t k_stride_token, int64_t k_stride_head,
+                             int64_t v_stride_token, int64_t v_stride_head,
+                             int64_t kc_stride_page, int64_t kc_stride_offset,
+                             int64_t kc_stride_head, int64_t vc_stride_page,
+                             int64_t vc_stride_offset, int64_t vc_stride_head, int64_t batch,
+                             int64_t size_limit, int64_t page_size, const float* inv_k,
+                             const float* inv_v, int fmt, int64_t* first_bad,
+                             uint64_t* bad_count) {
     int64_t written = 0;
     float ik = inv_k ? *inv_k : 1.0f;
     float iv = inv_v ? *inv_v : 1.0f;
@@ -260,13 +308,49 @@ int64_t oracle_fp8_paged(const uint8_t* k, const uint8_t* v, uint8_t* k_cache,
         int64_t off = loc % page_size;
         store_fp8_row(k, k_stride_token, k_stride_head, t, k_cache, kc_stride_page,
                       kc_stride_offset, kc_stride_head, page, off, num_heads, head_dim,
-                      src_is_fp16, ik);
+                      src_is_fp16, ik, fmt);
         store_fp8_row(v, v_stride_token, v_stride_head, t, v_cache, vc_stride_page,
                       vc_stride_offset, vc_stride_head, page, off, num_heads, head_dim,
-                      src_is_fp16, iv);
+                      src_is_fp16, iv, fmt);
         ++written;
     }
     return written;
+}
+
+/* e4m3fn caches (the fused kernel's format). */
+int64_t oracle_fp8_paged(const uint8_t* k, const uint8_t* v, uint8_t* k_cache,
+                         uint8_t* v_cache, const void* indices, int idx_is_i64,
+                         int64_t idx_stride, int src_is_fp16, int64_t num_heads,
+                         int64_t head_dim, int64_t k_stride_token, int64_t k_stride_head,
+                         int64_t v_stride_token, int64_t v_stride_head,
+                         int64_t kc_stride_page, int64_t kc_stride_offset,
+                         int64_t kc_stride_head, int64_t vc_stride_page,
+                         int64_t vc_stride_offset, int64_t vc_stride_head, int64_t batch,
+                         int64_t size_limit, int64_t page_size, const float* inv_k,
+                         const float* inv_v, int64_t* first_bad, uint64_t* bad_count) {
+    return fp8_paged_fmt(k, v, k_cache, v_cache, indices, idx_is_i64, idx_stride, src_is_fp16,
+                         num_heads, head_dim, k_stride_token, k_stride_head, v_stride_token,
+                         v_stride_head, kc_stride_page, kc_stride_offset, kc_stride_head,
+                         vc_stride_page, vc_stride_offset, vc_stride_head, batch, size_limit,
+                         page_size, inv_k, inv_v, FMT_E4M3FN, first_bad, bad_count);
+}
+
+/* e5m2 caches, same arguments. */
+int64_t oracle_fp8_paged_e5m2(const uint8_t* k, const uint8_t* v, uint8_t* k_cache,
+                              uint8_t* v_cache, const void* indices, int idx_is_i64,
+                              int64_t idx_stride, int src_is_fp16, int64_t num_heads,
+                              int64_t head_dim, int64_t k_stride_token, int64_t k_stride_head,
+                              int64_t v_stride_token, int64_t v_stride_head,
+                              int64_t kc_stride_page, int64_t kc_stride_offset,
+                              int64_t kc_stride_head, int64_t vc_stride_page,
+                              int64_t vc_stride_offset, int64_t vc_stride_head, int64_t batch,
+                              int64_t size_limit, int64_t page_size, const float* inv_k,
+                              const float* inv_v, int64_t* first_bad, uint64_t* bad_count) {
+    return fp8_paged_fmt(k, v, k_cache, v_cache, indices, idx_is_i64, idx_stride, src_is_fp16,
+                         num_heads, head_dim, k_stride_token, k_stride_head, v_stride_token,
+                         v_stride_head, kc_stride_page, kc_stride_offset, kc_stride_head,
+                         vc_stride_page, vc_stride_offset, vc_stride_head, batch, size_limit,
+                         page_size, inv_k, inv_v, FMT_E5M2, first_bad, bad_count);
 }
 
 /* ---------------------------------------------------------------------- */

@@ -113,6 +113,20 @@ def _decode(lib, src):
             and np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32)))
 
 
+def _e5m2(lib):
+    y, want = [], []
+    import os
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "e5m2_pins.txt")):
+        if line.strip() and not line.startswith("#"):
+            a, b = line.split()[:2]
+            y.append(int(a, 16))
+            want.append(int(b, 16))
+    yv = np.array(y, dtype=np.uint32).view(np.float32)
+    return (np.array_equal(oracle.e5m2(yv, lib=lib), np.array(want, dtype=np.uint8))
+            and np.array_equal(oracle.quantize(ALL16, "fp16", kvgen.INV_K_BITS, lib=lib, fmt="e5m2"),
+                               _ref.expected_codes(ALL16, "fp16", kvgen.INV_K_BITS, "e5m2")))
+
+
 CHECKS = {
     "decode_bf16": lambda lib: _decode(lib, "bf16"),
     "decode_fp16": lambda lib: _decode(lib, "fp16"),
@@ -122,6 +136,7 @@ CHECKS = {
     "copy_store": _copy,
     "fp8_store": _fp8,
     "fp8_dynamic": _dynamic,
+    "e5m2": _e5m2,
 }
 
 

@@ -29,10 +29,37 @@ def e4m3fn_decode(code: int) -> float:
 TABLE = np.array([e4m3fn_decode(c) for c in range(0x7F)], dtype=np.float64)
 
 
+def e5m2_decode(code: int) -> float:
+    """Value of an e5m2 code, from the format definition (1 sign, 5 exponent
+    bits with bias 15, 2 mantissa bits; exponent 31 is inf / NaN)."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 2) & 0x1F
+    m = code & 0x3
+    if e == 0x1F:
+        return s * float("inf") if m == 0 else float("nan")
+    if e == 0:
+        return s * m * 2.0 ** -16
+    return s * (1.0 + m / 4.0) * 2.0 ** (e - 15)
+
+
+# Non-negative finite e5m2 values, indexed by code 0x00..0x7B.
+TABLE_E5M2 = np.array([e5m2_decode(c) for c in range(0x7C)], dtype=np.float64)
+
+
+def nearest_e5m2(y: np.ndarray, nan_sign_from: np.ndarray | None = None) -> np.ndarray:
+    """Nearest finite e5m2 code (ties to the even code, sign kept, NaN ->
+    0x7F | sign, infinities to the largest finite)."""
+    return _nearest(y, TABLE_E5M2, nan_sign_from)
+
+
 def nearest_e4m3fn(y: np.ndarray, nan_sign_from: np.ndarray | None = None) -> np.ndarray:
     """Nearest finite e4m3fn code to each fp32 value; on a tie the code whose
     lowest bit is 0; sign kept (so values that round to zero give +-0);
     NaN -> 0x7F with the sign of ``nan_sign_from`` (default: of y)."""
+    return _nearest(y, TABLE, nan_sign_from)
+
+
+def _nearest(y, table, nan_sign_from):
     y = np.asarray(y, dtype=np.float32).ravel()
     out = np.empty(y.size, dtype=np.uint8)
     sign = np.signbit(y)
@@ -49,17 +76,17 @@ def nearest_e4m3fn(y: np.ndarray, nan_sign_from: np.ndarray | None = None) -> np
         aa = a[s:s + step].copy()
         bad = isnan[s:s + step] | isinf[s:s + step]
         aa[bad] = 0.0
-        # Every table value is <= 448, so for any |y| above 1024 the order of
-        # the distances is the same as for 1024; clamping keeps the float64
-        # differences exact (no large-minus-small cancellation).
-        aa = np.minimum(aa, 1024.0)
-        d = np.abs(aa[:, None] - TABLE[None, :])
+        # Every table value is <= its largest entry, so for any |y| above
+        # twice that the order of the distances is the same as at twice it;
+        # clamping keeps the float64 differences exact (no cancellation).
+        aa = np.minimum(aa, 2.0 * table[-1])
+        d = np.abs(aa[:, None] - table[None, :])
         lo = np.argmin(d, axis=1)
         dmin = d[np.arange(lo.size), lo]
-        nxt = np.minimum(lo + 1, TABLE.size - 1)
-        tie = (lo + 1 < TABLE.size) & (d[np.arange(lo.size), nxt] == dmin)
+        nxt = np.minimum(lo + 1, table.size - 1)
+        tie = (lo + 1 < table.size) & (d[np.arange(lo.size), nxt] == dmin)
         code = np.where(tie & (lo % 2 == 1), lo + 1, lo)
-        code = np.where(isinf[s:s + step], 0x7E, code)
+        code = np.where(isinf[s:s + step], table.size - 1, code)
         out[s:s + step] = code.astype(np.uint8)
     out = np.where(sign, out | 0x80, out).astype(np.uint8)
     out = np.where(isnan, np.where(nsrc, 0xFF, 0x7F), out).astype(np.uint8)
@@ -91,9 +118,15 @@ def scaled(bits: np.ndarray, src_dtype: str, inv_bits) -> tuple:
     return x, y
 
 
-def expected_codes(bits: np.ndarray, src_dtype: str, inv_bits) -> np.ndarray:
+def expected_codes(bits: np.ndarray, src_dtype: str, inv_bits, fmt: str = "e4m3fn") -> np.ndarray:
     x, y = scaled(bits, src_dtype, inv_bits)
-    return nearest_e4m3fn(y, nan_sign_from=x).reshape(np.shape(bits))
+    # an invalid product (inf * 0) is the negative default NaN
+    bad = np.isnan(y) & ~np.isnan(x)
+    y = y.copy()
+    y[bad] = np.array([0xFFC00000], dtype=np.uint32).view(np.float32)[0]
+    src = np.where(bad, y, x)
+    f = nearest_e5m2 if fmt == "e5m2" else nearest_e4m3fn
+    return f(y, nan_sign_from=src).reshape(np.shape(bits))
 
 
 # ---------------------------------------------------------------------------

@@ -42,6 +42,11 @@ MUTANTS = {
     "index_stride_ignored": ("read_index(indices, idx_is_i64, t * idx_stride)",
                              "read_index(indices, idx_is_i64, t)"),
     "first_bad_keeps_max": ("t < *first_bad", "t > *first_bad"),
+    "e5m2_overflow_to_inf": ("if (a > 57344.0) return (uint8_t)(0x7B | s);",
+                             "if (a > 57344.0) return (uint8_t)(0x7C | s);"),
+    "e5m2_subnormal_scale": ("round_half_even(a * 65536.0)", "round_half_even(a * 32768.0)"),
+    "e5m2_bias": ("((e + 15) << 2)", "((e + 16) << 2)"),
+    "e5m2_no_carry": ("if (m == 8.0) {", "if (m == 9.0) {"),
     "dyn_no_scale_floor": ("if (scale < FLT_MIN) scale = FLT_MIN;", ""),
     "dyn_inverse_in_one_step": ("float inv = 1.0f / scale;", "float inv = 448.0f / amax;"),
     "dyn_signed_amax": ("float a = fabsf(src_to_float(bits, src_is_fp16));",
