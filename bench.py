@@ -316,6 +316,35 @@ def bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh, n=50):
             "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         del ks, vs
+    # the same store into e5m2 caches, given scales
+    ik = torch.tensor([0.4], dtype=torch.float32, device=dev)
+    iv = torch.tensor([1.0 / 1.7], dtype=torch.float32, device=dev)
+
+    def call_e5m2(s):
+        st = kv.kvstore_fp8_paged_e5m2(
+            k4[s].data_ptr(), v4[s].data_ptr(), kc.data_ptr(), vc.data_ptr(), i4[s].data_ptr(),
+            kv.IDX_I32, 1, kv.SRC_BF16, H, D, c4.in_stride_bytes, 2 * D, c4.in_stride_bytes,
+            2 * D, P * R, R, D, P * R, R, D, c4.num_tokens, c4.slots, P, ik.data_ptr(),
+            iv.data_ptr(), sh)
+        if st:
+            raise kv.KVStoreError(st, "kvstore_fp8_paged_e5m2")
+
+    for i in range(5):
+        call_e5m2(i % S)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(torch.cuda.current_stream())
+    for i in range(n):
+        call_e5m2(i % S)
+    e1.record(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    b = c4.algorithmic_bytes()
+    out["fp8_e5m2"] = {
+        "workload": "fused FP8 paged store into e5m2 caches (16384 tok, 8x128 bf16, int32, "
+                    "page 64, inv scales 1/2.5 1/1.7)",
+        "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+        "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     st, _, _ = kv.kvstore_check_error(sh)
     assert st == kv.OK
     del kc, vc

@@ -9,6 +9,7 @@ pointers are ints, strides in bytes unless stated):
 
     kvstore_copy(...)        -> status
     kvstore_fp8_paged(...)   -> status
+    kvstore_fp8_paged_e5m2(...) -> status
     kvstore_fp8_paged_dynamic(...) -> status
     kvstore_check_error(stream) -> (status, first_bad_token, bad_count)
     kvstore_strerror(status) -> str
@@ -23,7 +24,9 @@ Tensor level (torch tensors on the GPU; the current stream is used):
         sglang "trtllm_fp8_kv_kernel.py" fused_fp8_set_kv_buffer: k/v
         [T, H, D] or [T, H*D] bf16/fp16; caches uint8 (e4m3fn bytes) or
         float8_e4m3fn, flat [slots, H, D] or paged [pages, page_size, H, D];
-        inverse scales as fp32 device tensors (one element) or None.
+        inverse scales as fp32 device tensors (one element) or None.  Caches
+        of dtype float8_e5m2 (or fp8_format="e5m2") get e5m2 codes; uint8 and
+        float8_e4m3fn caches get e4m3fn codes.
     store_kv_fp8_paged_dynamic(k, v, k_cache, v_cache, cache_loc,
                                k_scale_cache, v_scale_cache, per_head=False,
                                page_size=16, size_limit=None)
@@ -53,8 +56,8 @@ SRC_FP16 = 1
 SCALE_PER_TOKEN = 0
 SCALE_PER_TOKEN_HEAD = 1
 
-EXPORTED = ("kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_dynamic",
-            "kvstore_check_error", "kvstore_strerror")
+EXPORTED = ("kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_e5m2",
+            "kvstore_fp8_paged_dynamic", "kvstore_check_error", "kvstore_strerror")
 
 
 class KVStoreError(RuntimeError):
@@ -76,6 +79,8 @@ def _load():
                                       i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, u32, i64,
                                       i64, vp, vp, vp]
     lib.kvstore_fp8_paged.restype = i32
+    lib.kvstore_fp8_paged_e5m2.argtypes = lib.kvstore_fp8_paged.argtypes
+    lib.kvstore_fp8_paged_e5m2.restype = i32
     lib.kvstore_fp8_paged_dynamic.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, C.c_int32,
                                               C.c_int32, i64, i64, i64, i64, i64, i64, i64, i64,
                                               i64, i64, vp, vp, i32, i64, i64, i64, i64, i64, i64,
@@ -116,6 +121,22 @@ def kvstore_fp8_paged(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, sr
                                   kc_stride_head_bytes, vc_stride_page_bytes,
                                   vc_stride_offset_bytes, vc_stride_head_bytes, batch,
                                   size_limit, page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream)
+
+
+def kvstore_fp8_paged_e5m2(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype,
+                           num_heads, head_dim, k_stride_token_bytes, k_stride_head_bytes,
+                           v_stride_token_bytes, v_stride_head_bytes, kc_stride_page_bytes,
+                           kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
+                           vc_stride_offset_bytes, vc_stride_head_bytes, batch, size_limit,
+                           page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream=None) -> int:
+    return _lib.kvstore_fp8_paged_e5m2(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride,
+                                       src_dtype, num_heads, head_dim, k_stride_token_bytes,
+                                       k_stride_head_bytes, v_stride_token_bytes,
+                                       v_stride_head_bytes, kc_stride_page_bytes,
+                                       kc_stride_offset_bytes, kc_stride_head_bytes,
+                                       vc_stride_page_bytes, vc_stride_offset_bytes,
+                                       vc_stride_head_bytes, batch, size_limit, page_size,
+                                       inv_k_scale_ptr, inv_v_scale_ptr, stream)
 
 
 def kvstore_fp8_paged_dynamic(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype,
@@ -246,10 +267,16 @@ def _input_strides(x, H, D):
 
 
 def store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16, inv_k_scale=None,
-                       inv_v_scale=None, size_limit=None, stream=None) -> None:
-    """Fused e4m3fn quantise + paged store (scales are fp32 *inverse* scales
-    on the device; None means unscaled)."""
+                       inv_v_scale=None, size_limit=None, stream=None, fp8_format=None) -> None:
+    """Fused FP8 quantise + paged store (scales are fp32 *inverse* scales on
+    the device; None means unscaled).  fp8_format "e4m3fn" or "e5m2"; by
+    default e5m2 for float8_e5m2 caches, else e4m3fn."""
     torch = _torch()
+    if fp8_format is None:
+        fp8_format = "e5m2" if k_cache.dtype == torch.float8_e5m2 else "e4m3fn"
+    if fp8_format not in ("e4m3fn", "e5m2"):
+        raise ValueError(f"unknown fp8_format {fp8_format!r}")
+    entry = kvstore_fp8_paged_e5m2 if fp8_format == "e5m2" else kvstore_fp8_paged
     _check_cuda(k, v, k_cache, v_cache, cache_loc)
     if k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16:
         src = SRC_BF16
@@ -275,13 +302,12 @@ def store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16, inv_k_sc
             raise TypeError("inverse scales must be one-element fp32 GPU tensors")
         ptrs.append(s.data_ptr())
     limit = slots if size_limit is None else int(size_limit)
-    st = kvstore_fp8_paged(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                           cache_loc.data_ptr(), _idx_code(cache_loc),
-                           cache_loc.stride(0) if T else 1, src, H, D, ks[0], ks[1], vs[0], vs[1],
-                           kcs[0], kcs[1], kcs[2], vcs[0], vcs[1], vcs[2], T, limit, page_size,
-                           ptrs[0], ptrs[1], _stream_handle(stream))
+    st = entry(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+               cache_loc.data_ptr(), _idx_code(cache_loc), cache_loc.stride(0) if T else 1, src,
+               H, D, ks[0], ks[1], vs[0], vs[1], kcs[0], kcs[1], kcs[2], vcs[0], vcs[1], vcs[2],
+               T, limit, page_size, ptrs[0], ptrs[1], _stream_handle(stream))
     if st != OK:
-        raise KVStoreError(st, "kvstore_fp8_paged")
+        raise KVStoreError(st, entry.__name__)
 
 
 def _scale_strides(sc, per_head, H, page_size):

@@ -250,20 +250,19 @@ __device__ __forceinline__ float f16_hi(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
 }
 
-// fp32 product, then clamp to the largest finite e4m3fn magnitude.  A NaN
-// input is its own product (keeping its sign, whichever operand the multiply
-// would return); a NaN fails the comparison and passes through; infinities
-// clamp.
-__device__ __forceinline__ float scale_sat(float x, float inv) {
-  const float y = (x != x) ? x : __fmul_rn(x, inv);
-  return (__builtin_fabsf(y) > 448.0f) ? __builtin_copysignf(448.0f, y) : y;
+// Largest finite magnitude of the FP8 storage format: e4m3fn 448, e5m2 57344.
+template <bool kE5M2>
+__device__ __forceinline__ constexpr float fp8_max() {
+  return kE5M2 ? 57344.0f : 448.0f;
 }
 
-// 0x80 in every byte of w that equals 0xFF, 0 elsewhere.  (b & 0x7F) + 1
-// reaches 0x80 only when the low seven bits are all set, and never carries
-// into the next byte.
-__device__ __forceinline__ uint32_t ff_bytes(uint32_t w) {
-  return ((w & 0x7F7F7F7Fu) + 0x01010101u) & w & 0x80808080u;
+// fp32 product, then clamp to the largest finite magnitude.  A NaN input is
+// its own product (keeping its sign, whichever operand the multiply would
+// return); a NaN fails the comparison and passes through; infinities clamp.
+template <bool kE5M2>
+__device__ __forceinline__ float scale_sat(float x, float inv) {
+  const float y = (x != x) ? x : __fmul_rn(x, inv);
+  return (__builtin_fabsf(y) > fp8_max<kE5M2>()) ? __builtin_copysignf(fp8_max<kE5M2>(), y) : y;
 }
 
 // Sign bits of four fp32 values, one per byte (bit 7 of byte i = sign of i).
@@ -272,17 +271,37 @@ __device__ __forceinline__ uint32_t sign_bytes(float a, float b, float c, float 
          ((__float_as_uint(c) >> 8) & 0xFF0000u) | (__float_as_uint(d) & 0xFF000000u);
 }
 
-// Four saturated fp32 values -> four e4m3fn bytes (a first in the low byte),
-// with the hardware's round-to-nearest-even packed conversion.  The converter
-// writes every NaN as 0xFF; a NaN keeps its own sign here (0x7F | sign).  The
-// inputs are already clamped to +-448 (at most 0x7E / 0xFE), so a 0xFF byte
-// can only come from a NaN.
-__device__ __forceinline__ uint32_t pack_e4m3(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+// Hardware round-to-nearest-even packed conversion of two fp32 values into
+// the low (hi = false) or high half of a word.
+template <bool kE5M2>
+__device__ __forceinline__ int cvt_pk(float a, float b, int old, bool hi) {
+  if constexpr (kE5M2)
+    return hi ? __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, true)
+              : __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, false);
+  else
+    return hi ? __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, true)
+              : __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, false);
+}
+
+// Four saturated fp32 values -> four FP8 bytes (a first in the low byte).
+// The inputs are already clamped to the largest finite magnitude, so a byte
+// whose magnitude bits exceed the largest finite code (e4m3fn 0x7E, e5m2
+// 0x7B) can only come from a NaN; the converter's NaN code is replaced by
+// 0x7F | sign (the gfx950 converter writes every e4m3fn NaN as 0xFF).
+template <bool kE5M2>
+__device__ __forceinline__ uint32_t pack_fp8(float a, float b, float c, float d) {
+  int w = cvt_pk<kE5M2>(a, b, 0, false);
+  w = cvt_pk<kE5M2>(c, d, w, true);
   uint32_t u = (uint32_t)w;
-  const uint32_t nan = ff_bytes(u);
-  if (nan) u ^= nan & ~sign_bytes(a, b, c, d);
+  // 0x80 in each byte whose low seven bits exceed the largest finite code:
+  // adding (0x7F - max) carries into bit 7 exactly then, never into the next byte.
+  constexpr uint32_t bump = kE5M2 ? 0x04040404u : 0x01010101u;
+  const uint32_t nan = ((u & 0x7F7F7F7Fu) + bump) & 0x80808080u;
+  if (nan) {
+    const uint32_t bytes = (nan >> 7) * 0xFFu;
+    const uint32_t code = (0x7F7F7F7Fu | (sign_bytes(a, b, c, d) & 0x80808080u)) & bytes;
+    u = (u & ~bytes) | code;
+  }
   return u;
 }
 
@@ -302,8 +321,9 @@ __device__ __forceinline__ bool any_nan16(u32x4 a, u32x4 b) {
 
 // Same result as quantize16 when no product can be NaN (no NaN input, scale
 // finite and non-zero): the clamp is one v_med3_f32 and no NaN fix-up is needed.
-template <bool kFp16>
+template <bool kFp16, bool kE5M2>
 __device__ __forceinline__ u32x4 quantize16_no_nan(u32x4 a, u32x4 b, float inv) {
+  constexpr float M = fp8_max<kE5M2>();
   u32x4 out;
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -315,22 +335,22 @@ __device__ __forceinline__ u32x4 quantize16_no_nan(u32x4 a, u32x4 b, float inv) 
     } else {
       e0 = bf16_lo(w0); e1 = bf16_hi(w0); e2 = bf16_lo(w1); e3 = bf16_hi(w1);
     }
-    e0 = __builtin_amdgcn_fmed3f(__fmul_rn(e0, inv), -448.0f, 448.0f);
-    e1 = __builtin_amdgcn_fmed3f(__fmul_rn(e1, inv), -448.0f, 448.0f);
-    e2 = __builtin_amdgcn_fmed3f(__fmul_rn(e2, inv), -448.0f, 448.0f);
-    e3 = __builtin_amdgcn_fmed3f(__fmul_rn(e3, inv), -448.0f, 448.0f);
-    int q = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
-    q = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, q, true);
+    e0 = __builtin_amdgcn_fmed3f(__fmul_rn(e0, inv), -M, M);
+    e1 = __builtin_amdgcn_fmed3f(__fmul_rn(e1, inv), -M, M);
+    e2 = __builtin_amdgcn_fmed3f(__fmul_rn(e2, inv), -M, M);
+    e3 = __builtin_amdgcn_fmed3f(__fmul_rn(e3, inv), -M, M);
+    int q = cvt_pk<kE5M2>(e0, e1, 0, false);
+    q = cvt_pk<kE5M2>(e2, e3, q, true);
     out[i] = (uint32_t)q;
   }
   return out;
 }
 
-// 16 source elements (two 16-byte vectors) -> 16 e4m3fn bytes.  scale_ok:
-// the inverse scale is finite and non-zero (wave-uniform).
-template <bool kFp16>
+// 16 source elements (two 16-byte vectors) -> 16 FP8 bytes.  scale_ok: the
+// inverse scale is finite and non-zero (wave-uniform).
+template <bool kFp16, bool kE5M2>
 __device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv, bool scale_ok) {
-  if (scale_ok && !any_nan16<kFp16>(a, b)) return quantize16_no_nan<kFp16>(a, b, inv);
+  if (scale_ok && !any_nan16<kFp16>(a, b)) return quantize16_no_nan<kFp16, kE5M2>(a, b, inv);
   u32x4 out;
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -342,8 +362,8 @@ __device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv, bool sc
     } else {
       e0 = bf16_lo(w0); e1 = bf16_hi(w0); e2 = bf16_lo(w1); e3 = bf16_hi(w1);
     }
-    out[i] = pack_e4m3(scale_sat(e0, inv), scale_sat(e1, inv), scale_sat(e2, inv),
-                       scale_sat(e3, inv));
+    out[i] = pack_fp8<kE5M2>(scale_sat<kE5M2>(e0, inv), scale_sat<kE5M2>(e1, inv),
+                             scale_sat<kE5M2>(e2, inv), scale_sat<kE5M2>(e3, inv));
   }
   return out;
 }
@@ -367,7 +387,7 @@ __device__ __forceinline__ void unit_offsets(uint32_t u, uint32_t units_per_head
 
 // Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = slices of
 // kPasses * 64 units.  Each lane handles kPasses units of K and of V.
-template <int kPasses, bool kFlat, bool kFp16, typename IdxT>
+template <int kPasses, bool kFlat, bool kFp16, bool kE5M2, typename IdxT>
 __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const Fp8Params p) {
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
@@ -427,8 +447,8 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
   for (int i = 0; i < kPasses; ++i) {
     const uint32_t u = (slice * kPasses + i) * kWave + lane;
     if (u < p.units) {
-      store16_sc1(kd, kdo[i], quantize16<kFp16>(ka[i], kb[i], inv_k, k_ok));
-      store16_sc1(vd, vdo[i], quantize16<kFp16>(va[i], vb[i], inv_v, v_ok));
+      store16_sc1(kd, kdo[i], quantize16<kFp16, kE5M2>(ka[i], kb[i], inv_k, k_ok));
+      store16_sc1(vd, vdo[i], quantize16<kFp16, kE5M2>(va[i], vb[i], inv_v, v_ok));
     }
   }
 }
@@ -567,8 +587,8 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
       const float ik = 1.0f / sk, iv = 1.0f / sv;
       // ik, iv are finite and non-zero unless a group holds an infinity
       const bool k_ok = ik != 0.0f, v_ok = iv != 0.0f;
-      store16_sc1(kd, kdo[i], quantize16<kFp16>(ka[i], kb[i], ik, k_ok));
-      store16_sc1(vd, vdo[i], quantize16<kFp16>(va[i], vb[i], iv, v_ok));
+      store16_sc1(kd, kdo[i], quantize16<kFp16, false>(ka[i], kb[i], ik, k_ok));
+      store16_sc1(vd, vdo[i], quantize16<kFp16, false>(va[i], vb[i], iv, v_ok));
       // One lane per group writes its scale: the first lane of each head
       // (per head, g < num_heads), or unit 0 alone (per token, g = 0).
       if (d.per_head ? (u & (d.group_lanes - 1)) == 0 : u == 0) {
@@ -657,28 +677,34 @@ int launch_copy(const CopyParams& p, int vw, hipStream_t stream) {
   return launch_copy_vw<4, IdxT>(p, stream);
 }
 
-template <int kPasses, bool kFlat, bool kFp16>
+template <int kPasses, bool kFlat, bool kFp16, bool kE5M2>
 int launch_fp8_idx(const Fp8Params& p, bool i64, dim3 grid, hipStream_t stream) {
   const dim3 block(kBlockThreads);
   if (i64)
-    hipLaunchKernelGGL((kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, int64_t>), grid, block,
-                       0, stream, p);
+    hipLaunchKernelGGL((kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, kE5M2, int64_t>), grid,
+                       block, 0, stream, p);
   else
-    hipLaunchKernelGGL((kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, int32_t>), grid, block,
-                       0, stream, p);
+    hipLaunchKernelGGL((kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, kE5M2, int32_t>), grid,
+                       block, 0, stream, p);
   return launch_status();
 }
 
-template <int kPasses>
-int launch_fp8_passes(const Fp8Params& p, bool flat, bool fp16, bool i64, dim3 grid,
-                      hipStream_t stream) {
+template <int kPasses, bool kE5M2>
+int launch_fp8_fmt(const Fp8Params& p, bool flat, bool fp16, bool i64, dim3 grid,
+                   hipStream_t stream) {
   if (flat)
-    return fp16 ? launch_fp8_idx<kPasses, true, true>(p, i64, grid, stream)
-                : launch_fp8_idx<kPasses, true, false>(p, i64, grid, stream);
-  return fp16 ? launch_fp8_idx<kPasses, false, true>(p, i64, grid, stream)
-              : launch_fp8_idx<kPasses, false, false>(p, i64, grid, stream);
+    return fp16 ? launch_fp8_idx<kPasses, true, true, kE5M2>(p, i64, grid, stream)
+                : launch_fp8_idx<kPasses, true, false, kE5M2>(p, i64, grid, stream);
+  return fp16 ? launch_fp8_idx<kPasses, false, true, kE5M2>(p, i64, grid, stream)
+              : launch_fp8_idx<kPasses, false, false, kE5M2>(p, i64, grid, stream);
 }
 
+template <int kPasses>
+int launch_fp8_passes(const Fp8Params& p, bool flat, bool fp16, bool i64, bool e5m2, dim3 grid,
+                      hipStream_t stream) {
+  return e5m2 ? launch_fp8_fmt<kPasses, true>(p, flat, fp16, i64, grid, stream)
+              : launch_fp8_fmt<kPasses, false>(p, flat, fp16, i64, grid, stream);
+}
 
 template <int kPasses, bool kFlat, bool kFp16>
 int launch_dyn_idx(const Fp8DynParams& d, bool i64, dim3 grid, hipStream_t stream) {
@@ -804,6 +830,46 @@ bool fp8_flat(const Fp8Params& p, int32_t head_dim) {
          p.kc_stride_head == head_dim && p.vc_stride_head == head_dim;
 }
 
+// The fused store with given per-tensor inverse scales, into e4m3fn or e5m2
+// caches.
+int fp8_paged_store(bool e5m2, const void* k, const void* v, void* k_cache, void* v_cache,
+                    const void* indices, int idx_dtype, int64_t idx_stride, int src_dtype,
+                    int32_t num_heads, int32_t head_dim, int64_t k_stride_token_bytes,
+                    int64_t k_stride_head_bytes, int64_t v_stride_token_bytes,
+                    int64_t v_stride_head_bytes, int64_t kc_stride_page_bytes,
+                    int64_t kc_stride_offset_bytes, int64_t kc_stride_head_bytes,
+                    int64_t vc_stride_page_bytes, int64_t vc_stride_offset_bytes,
+                    int64_t vc_stride_head_bytes, uint32_t batch, int64_t size_limit,
+                    int64_t page_size, const float* inv_k_scale_ptr, const float* inv_v_scale_ptr,
+                    hipStream_t stream) {
+  if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
+  if (src_dtype != KVSTORE_SRC_BF16 && src_dtype != KVSTORE_SRC_FP16) return KVSTORE_ERR_DTYPE;
+  if (batch == 0) return KVSTORE_OK;
+  Fp8Params p;
+  const int st = fill_fp8_params(
+      p, k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, num_heads, head_dim,
+      k_stride_token_bytes, k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
+      kc_stride_page_bytes, kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
+      vc_stride_offset_bytes, vc_stride_head_bytes, batch, size_limit, page_size);
+  if (st != KVSTORE_OK) return st;
+  if (!aligned(inv_k_scale_ptr, 4) || !aligned(inv_v_scale_ptr, 4)) return KVSTORE_ERR_ALIGN;
+  p.inv_k = inv_k_scale_ptr;
+  p.inv_v = inv_v_scale_ptr;
+  const bool flat = fp8_flat(p, head_dim);
+  const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
+  const bool i64 = idx_dtype == KVSTORE_IDX_I64;
+
+  // Units of 16 elements per lane: up to 2 per lane per tensor in one wave
+  // (32 B of K + 32 B of V loaded per unit), wider rows split over blockIdx.y.
+  const int64_t waves_units = ceil_div(p.units, kWave);
+  const int passes = waves_units >= 2 ? 2 : 1;
+  const int64_t slices = ceil_div(waves_units, passes);
+  if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
+  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), (uint32_t)slices);
+  return passes == 2 ? launch_fp8_passes<2>(p, flat, fp16, i64, e5m2, grid, stream)
+                     : launch_fp8_passes<1>(p, flat, fp16, i64, e5m2, grid, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -857,32 +923,30 @@ int kvstore_fp8_paged(const void* k, const void* v, void* k_cache, void* v_cache
                       int64_t vc_stride_head_bytes, uint32_t batch, int64_t size_limit,
                       int64_t page_size, const float* inv_k_scale_ptr,
                       const float* inv_v_scale_ptr, hipStream_t stream) {
-  if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
-  if (src_dtype != KVSTORE_SRC_BF16 && src_dtype != KVSTORE_SRC_FP16) return KVSTORE_ERR_DTYPE;
-  if (batch == 0) return KVSTORE_OK;
-  Fp8Params p;
-  const int st = fill_fp8_params(
-      p, k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, num_heads, head_dim,
-      k_stride_token_bytes, k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
-      kc_stride_page_bytes, kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
-      vc_stride_offset_bytes, vc_stride_head_bytes, batch, size_limit, page_size);
-  if (st != KVSTORE_OK) return st;
-  if (!aligned(inv_k_scale_ptr, 4) || !aligned(inv_v_scale_ptr, 4)) return KVSTORE_ERR_ALIGN;
-  p.inv_k = inv_k_scale_ptr;
-  p.inv_v = inv_v_scale_ptr;
-  const bool flat = fp8_flat(p, head_dim);
-  const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
-  const bool i64 = idx_dtype == KVSTORE_IDX_I64;
+  return fp8_paged_store(false, k, v, k_cache, v_cache, indices, idx_dtype, idx_stride,
+                         src_dtype, num_heads, head_dim, k_stride_token_bytes,
+                         k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
+                         kc_stride_page_bytes, kc_stride_offset_bytes, kc_stride_head_bytes,
+                         vc_stride_page_bytes, vc_stride_offset_bytes, vc_stride_head_bytes,
+                         batch, size_limit, page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream);
+}
 
-  // Units of 16 elements per lane: up to 2 per lane per tensor in one wave
-  // (32 B of K + 32 B of V loaded per unit), wider rows split over blockIdx.y.
-  const int64_t waves_units = ceil_div(p.units, kWave);
-  const int passes = waves_units >= 2 ? 2 : 1;
-  const int64_t slices = ceil_div(waves_units, passes);
-  if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
-  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), (uint32_t)slices);
-  return passes == 2 ? launch_fp8_passes<2>(p, flat, fp16, i64, grid, stream)
-                     : launch_fp8_passes<1>(p, flat, fp16, i64, grid, stream);
+int kvstore_fp8_paged_e5m2(const void* k, const void* v, void* k_cache, void* v_cache,
+                           const void* indices, int idx_dtype, int64_t idx_stride, int src_dtype,
+                           int32_t num_heads, int32_t head_dim, int64_t k_stride_token_bytes,
+                           int64_t k_stride_head_bytes, int64_t v_stride_token_bytes,
+                           int64_t v_stride_head_bytes, int64_t kc_stride_page_bytes,
+                           int64_t kc_stride_offset_bytes, int64_t kc_stride_head_bytes,
+                           int64_t vc_stride_page_bytes, int64_t vc_stride_offset_bytes,
+                           int64_t vc_stride_head_bytes, uint32_t batch, int64_t size_limit,
+                           int64_t page_size, const float* inv_k_scale_ptr,
+                           const float* inv_v_scale_ptr, hipStream_t stream) {
+  return fp8_paged_store(true, k, v, k_cache, v_cache, indices, idx_dtype, idx_stride,
+                         src_dtype, num_heads, head_dim, k_stride_token_bytes,
+                         k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
+                         kc_stride_page_bytes, kc_stride_offset_bytes, kc_stride_head_bytes,
+                         vc_stride_page_bytes, vc_stride_offset_bytes, vc_stride_head_bytes,
+                         batch, size_limit, page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream);
 }
 
 int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void* v_cache,

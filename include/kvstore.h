@@ -1,7 +1,7 @@
 /*
  * libkvstore -- KV-cache store for MI355X (gfx950).
  *
- * Three store operations and their error reporting, as a plain C ABI.  Every
+ * Four store operations and their error reporting, as a plain C ABI.  Every
  * pointer argument of a store call is a DEVICE pointer owned by the caller
  * (for example a torch tensor's data pointer); the library never allocates,
  * frees or synchronises inside a store call.  Work is enqueued on the given
@@ -22,6 +22,8 @@
  *                         offset = loc % page_size; every element x of K (V)
  *                         becomes e4m3fn(x * inv_k) (e4m3fn(x * inv_v)) at
  *                         [page, offset, head, dim] of the K (V) cache.
+ *   kvstore_fp8_paged_e5m2 -- the same store into float8_e5m2 caches, which
+ *                         the page's unfused path also writes.
  *   kvstore_fp8_paged_dynamic -- the same store with per-token (or per token
  *                         and head) scales computed in the kernel, the step
  *                         the docstring of "trtllm_fp8_kv_kernel.py" lists as
@@ -152,6 +154,25 @@ int kvstore_fp8_paged(const void* k, const void* v, void* k_cache, void* v_cache
                       int64_t vc_stride_head_bytes, uint32_t batch, int64_t size_limit,
                       int64_t page_size, const float* inv_k_scale_ptr,
                       const float* inv_v_scale_ptr, hipStream_t stream);
+
+/*
+ * As kvstore_fp8_paged, into float8_e5m2 caches (the page's unfused path,
+ * _naive_fp8_set_kv_buffer in "trtllm_fp8_kv_kernel.py", stores into e5m2 as
+ * well as e4m3fn caches).  Same arguments and rules; each element becomes the
+ * nearest e5m2 value to x * inv (1 sign, 5 exponent bits with bias 15, 2
+ * mantissa bits), ties to even, saturating to +-57344 (infinities too), NaN
+ * -> 0x7F | sign.
+ */
+int kvstore_fp8_paged_e5m2(const void* k, const void* v, void* k_cache, void* v_cache,
+                           const void* indices, int idx_dtype, int64_t idx_stride, int src_dtype,
+                           int32_t num_heads, int32_t head_dim, int64_t k_stride_token_bytes,
+                           int64_t k_stride_head_bytes, int64_t v_stride_token_bytes,
+                           int64_t v_stride_head_bytes, int64_t kc_stride_page_bytes,
+                           int64_t kc_stride_offset_bytes, int64_t kc_stride_head_bytes,
+                           int64_t vc_stride_page_bytes, int64_t vc_stride_offset_bytes,
+                           int64_t vc_stride_head_bytes, uint32_t batch, int64_t size_limit,
+                           int64_t page_size, const float* inv_k_scale_ptr,
+                           const float* inv_v_scale_ptr, hipStream_t stream);
 
 /*
  * Fused FP8 (e4m3fn) quantise + paged store with dynamic scales.  The

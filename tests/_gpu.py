@@ -51,7 +51,7 @@ def run_copy(case, kc, vc, idx_dev=None, size_limit=None, batch=None, idx_stride
 
 
 def run_fp8(case, kc, vc, idx_dev=None, size_limit=None, kc_strides=None, vc_strides=None,
-            in_strides=None, k_dev=None, v_dev=None, batch=None, idx_stride=1):
+            in_strides=None, k_dev=None, v_dev=None, batch=None, idx_stride=1, fmt="e4m3fn"):
     """kvstore_fp8_paged through the C ABI for a kvgen fp8 case (contiguous
     [slots, H*D] byte caches unless strides are given)."""
     H, D, P = case.num_heads, case.head_dim, case.page_size
@@ -63,7 +63,8 @@ def run_fp8(case, kc, vc, idx_dev=None, size_limit=None, kc_strides=None, vc_str
     kcs = kc_strides or (P * row, row, D)
     vcs = vc_strides or kcs
     ik, iv = f32_dev(case.inv_k_bits), f32_dev(case.inv_v_bits)
-    st = kv.kvstore_fp8_paged(
+    entry = kv.kvstore_fp8_paged_e5m2 if fmt == "e5m2" else kv.kvstore_fp8_paged
+    st = entry(
         k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(), idx.data_ptr(),
         idx_code(case.indices), idx_stride, kv.SRC_FP16 if case.src_dtype == "fp16" else kv.SRC_BF16,
         H, D, ks[0], ks[1], ks[0], ks[1], kcs[0], kcs[1], kcs[2], vcs[0], vcs[1], vcs[2],

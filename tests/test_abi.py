@@ -39,8 +39,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
-        ["kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_dynamic", "kvstore_check_error",
-         "kvstore_strerror"])
+        ["kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_e5m2",
+         "kvstore_fp8_paged_dynamic", "kvstore_check_error", "kvstore_strerror"])
 
 
 def test_library_exports_every_declared_symbol(kv):
@@ -131,9 +131,9 @@ def _copy_call(kv, **over):
                            a["size_limit"], None)
 
 
-def _fp8_call(kv, **over):
+def _fp8_call(kv, _entry=None, **over):
     a = dict(FP8_OK, **over)
-    return kv.kvstore_fp8_paged(*[a[n] for n in (
+    return (_entry or kv.kvstore_fp8_paged)(*[a[n] for n in (
         "k", "v", "k_cache", "v_cache", "indices", "idx_dtype", "idx_stride", "src_dtype",
         "num_heads", "head_dim", "k_stride_token_bytes", "k_stride_head_bytes",
         "v_stride_token_bytes", "v_stride_head_bytes", "kc_stride_page_bytes",
@@ -155,6 +155,7 @@ def test_copy_rejects(kv, name, over, status):
 @pytest.mark.parametrize("name,over,status", FP8_BAD, ids=[c[0] for c in FP8_BAD])
 def test_fp8_rejects(kv, name, over, status):
     assert _fp8_call(kv, **over) == status
+    assert _fp8_call(kv, _entry=kv.kvstore_fp8_paged_e5m2, **over) == status
 
 
 @cpu_only
@@ -171,6 +172,7 @@ def test_valid_arguments_reach_the_runtime(kv):
     # With no GPU the launch itself fails: the call got past validation.
     assert _copy_call(kv) == kv.ERR_HIP
     assert _fp8_call(kv) == kv.ERR_HIP
+    assert _fp8_call(kv, _entry=kv.kvstore_fp8_paged_e5m2) == kv.ERR_HIP
     # 8- and 4-byte aligned rows and pointers are accepted by the copy
     assert _copy_call(kv, row_bytes=2040, k=A + 8) == kv.ERR_HIP
     assert _copy_call(kv, row_bytes=36, k_stride_bytes=36, v_stride_bytes=40,
