@@ -40,7 +40,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;                     // lanes per wavefront (CDNA)
 constexpr int kLaneBytes = 16;                // bytes per lane per access
 constexpr int kChunkBytes = kWave * kLaneBytes;  // 1 KiB per wave access
-constexpr int kWavesPerBlock = 4;             // fp8 kernel
+constexpr int kWavesPerBlock = 2;             // fp8 kernels
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kCopyWavesPerBlock = 2;         // copy kernel
 constexpr int kCopyBlockThreads = kWave * kCopyWavesPerBlock;
@@ -385,71 +385,83 @@ __device__ __forceinline__ void unit_offsets(uint32_t u, uint32_t units_per_head
   }
 }
 
-// Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = slices of
-// kPasses * 64 units.  Each lane handles kPasses units of K and of V.
+// One tensor (K or V) of one token, as the wave sees it.
+struct TensorView {
+  const uint8_t* src;   // this token's input row
+  int64_t src_head;
+  uint8_t* cache;
+  int64_t c_page, c_offset, c_head;
+  const float* inv;
+};
+
+__device__ __forceinline__ TensorView tensor_view(const Fp8Params& p, bool is_v, uint32_t token) {
+  TensorView t;
+  t.src = (is_v ? p.v : p.k) + (int64_t)token * (is_v ? p.v_stride_token : p.k_stride_token);
+  t.src_head = is_v ? p.v_stride_head : p.k_stride_head;
+  t.cache = is_v ? p.v_cache : p.k_cache;
+  t.c_page = is_v ? p.vc_stride_page : p.kc_stride_page;
+  t.c_offset = is_v ? p.vc_stride_offset : p.kc_stride_offset;
+  t.c_head = is_v ? p.vc_stride_head : p.kc_stride_head;
+  t.inv = is_v ? p.inv_v : p.inv_k;
+  return t;
+}
+
+// Byte offset of slot loc in a paged cache with the given page/offset strides.
+__device__ __forceinline__ int64_t slot_offset(const Fp8Params& p, int64_t loc, int64_t c_page,
+                                               int64_t c_offset) {
+  if (p.linear_pages) return loc * c_offset;
+  int64_t page, off;
+  if (p.page_shift >= 0) {
+    page = loc >> p.page_shift;
+    off = loc & (p.page_size - 1);
+  } else {
+    page = loc / p.page_size;
+    off = loc - page * p.page_size;
+  }
+  return page * c_page + off * c_offset;
+}
+
+// Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = 2 * slices:
+// bit 0 selects K (0) or V (1), the rest the slice of kPasses * 64 units.
+// K and V of a token go to separate waves: twice the waves of half the size
+// measured ~7% faster than one wave doing both.
 template <int kPasses, bool kFlat, bool kFp16, bool kE5M2, typename IdxT>
 __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const Fp8Params p) {
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
   if (token >= p.batch) return;
-  const uint32_t slice = blockIdx.y;
+  const bool is_v = (blockIdx.y & 1u) != 0;
+  const uint32_t slice = blockIdx.y >> 1;
 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
-  const float inv_k = p.inv_k ? *p.inv_k : 1.0f;
-  const float inv_v = p.inv_v ? *p.inv_v : 1.0f;
+  const TensorView t = tensor_view(p, is_v, token);
+  const float inv = t.inv ? *t.inv : 1.0f;
   // v_med3 drops NaN, so the single-instruction clamp is used only when no
   // product can be NaN: finite, non-zero scale and no NaN input.
-  const bool k_ok = __builtin_fabsf(inv_k) <= 3.40282347e38f && inv_k != 0.0f;
-  const bool v_ok = __builtin_fabsf(inv_v) <= 3.40282347e38f && inv_v != 0.0f;
+  const bool scale_ok = __builtin_fabsf(inv) <= 3.40282347e38f && inv != 0.0f;
 
-  const uint8_t* ks = p.k + (int64_t)token * p.k_stride_token;
-  const uint8_t* vs = p.v + (int64_t)token * p.v_stride_token;
-
-  u32x4 ka[kPasses], kb[kPasses], va[kPasses], vb[kPasses];
-  uint32_t kdo[kPasses], vdo[kPasses];
+  u32x4 a[kPasses], b[kPasses];
+  uint32_t dof[kPasses];
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
     const uint32_t u = (slice * kPasses + i) * kWave + lane;
     if (u < p.units) {
-      uint32_t kso, vso;
-      unit_offsets<kFlat>(u, p.units_per_head, p.k_stride_head, p.kc_stride_head, &kso, &kdo[i]);
-      unit_offsets<kFlat>(u, p.units_per_head, p.v_stride_head, p.vc_stride_head, &vso, &vdo[i]);
-      ka[i] = load16(ks, kso);
-      kb[i] = load16(ks, kso + 16u);
-      va[i] = load16(vs, vso);
-      vb[i] = load16(vs, vso + 16u);
+      uint32_t sof;
+      unit_offsets<kFlat>(u, p.units_per_head, t.src_head, t.c_head, &sof, &dof[i]);
+      a[i] = load16(t.src, sof);
+      b[i] = load16(t.src, sof + 16u);
     }
   }
 
   if (loc < 0 || loc >= p.size_limit) {
-    if (lane == 0 && slice == 0) report_bad_token(token);
+    if (lane == 0 && slice == 0 && !is_v) report_bad_token(token);
     return;
   }
-  int64_t k_slot, v_slot;
-  if (p.linear_pages) {
-    k_slot = loc * p.kc_stride_offset;
-    v_slot = loc * p.vc_stride_offset;
-  } else {
-    int64_t page, off;
-    if (p.page_shift >= 0) {
-      page = loc >> p.page_shift;
-      off = loc & (p.page_size - 1);
-    } else {
-      page = loc / p.page_size;
-      off = loc - page * p.page_size;
-    }
-    k_slot = page * p.kc_stride_page + off * p.kc_stride_offset;
-    v_slot = page * p.vc_stride_page + off * p.vc_stride_offset;
-  }
-  const __amdgpu_buffer_rsrc_t kd = row_rsrc(p.k_cache + k_slot);
-  const __amdgpu_buffer_rsrc_t vd = row_rsrc(p.v_cache + v_slot);
+  const __amdgpu_buffer_rsrc_t d = row_rsrc(t.cache + slot_offset(p, loc, t.c_page, t.c_offset));
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
     const uint32_t u = (slice * kPasses + i) * kWave + lane;
-    if (u < p.units) {
-      store16_sc1(kd, kdo[i], quantize16<kFp16, kE5M2>(ka[i], kb[i], inv_k, k_ok));
-      store16_sc1(vd, vdo[i], quantize16<kFp16, kE5M2>(va[i], vb[i], inv_v, v_ok));
-    }
+    if (u < p.units) store16_sc1(d, dof[i], quantize16<kFp16, kE5M2>(a[i], b[i], inv, scale_ok));
   }
 }
 
@@ -498,71 +510,54 @@ __device__ __forceinline__ float dyn_scale(float amax) {
   return __builtin_fmaxf(amax / 448.0f, 1.17549435e-38f);
 }
 
-// Grid: x = ceil(batch / kWavesPerBlock), one wave per token holding the
-// whole row: kPasses units of 16 elements per lane for K and for V.
+// Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = 2: K (0) or
+// V (1).  The wave holds the tensor's whole row: kPasses units of 16 elements
+// per lane.
 template <int kPasses, bool kFlat, bool kFp16, typename IdxT>
 __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(const Fp8DynParams d) {
   const Fp8Params& p = d.base;
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
   if (token >= p.batch) return;
+  const bool is_v = blockIdx.y != 0;
 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
-  const uint8_t* ks = p.k + (int64_t)token * p.k_stride_token;
-  const uint8_t* vs = p.v + (int64_t)token * p.v_stride_token;
+  const TensorView t = tensor_view(p, is_v, token);
 
-  u32x4 ka[kPasses], kb[kPasses], va[kPasses], vb[kPasses];
-  uint32_t kdo[kPasses], vdo[kPasses];
-  float km[kPasses], vm[kPasses];
+  u32x4 a[kPasses], b[kPasses];
+  uint32_t dof[kPasses];
+  float m[kPasses];
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
     const uint32_t u = i * kWave + lane;
-    km[i] = 0.0f;
-    vm[i] = 0.0f;
+    m[i] = 0.0f;
     if (u < p.units) {
-      uint32_t kso, vso;
-      unit_offsets<kFlat>(u, p.units_per_head, p.k_stride_head, p.kc_stride_head, &kso, &kdo[i]);
-      unit_offsets<kFlat>(u, p.units_per_head, p.v_stride_head, p.vc_stride_head, &vso, &vdo[i]);
-      ka[i] = load16(ks, kso);
-      kb[i] = load16(ks, kso + 16u);
-      va[i] = load16(vs, vso);
-      vb[i] = load16(vs, vso + 16u);
+      uint32_t sof;
+      unit_offsets<kFlat>(u, p.units_per_head, t.src_head, t.c_head, &sof, &dof[i]);
+      a[i] = load16(t.src, sof);
+      b[i] = load16(t.src, sof + 16u);
     }
   }
   // Every lane takes part in the shuffles below, so the bounds check comes after.
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
-    const uint32_t u = i * kWave + lane;
-    if (u < p.units) {
-      km[i] = amax16<kFp16>(ka[i], kb[i]);
-      vm[i] = amax16<kFp16>(va[i], vb[i]);
-    }
+    if (i * kWave + lane < p.units) m[i] = amax16<kFp16>(a[i], b[i]);
   }
   if (!d.per_head) {
     // one group: the whole row
-    float mk = km[0], mv = vm[0];
+    float mx = m[0];
 #pragma unroll
-    for (int i = 1; i < kPasses; ++i) {
-      mk = __builtin_fmaxf(mk, km[i]);
-      mv = __builtin_fmaxf(mv, vm[i]);
-    }
-    mk = group_max(mk, kWave);
-    mv = group_max(mv, kWave);
+    for (int i = 1; i < kPasses; ++i) mx = __builtin_fmaxf(mx, m[i]);
+    mx = group_max(mx, kWave);
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) {
-      km[i] = mk;
-      vm[i] = mv;
-    }
+    for (int i = 0; i < kPasses; ++i) m[i] = mx;
   } else {
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) {
-      km[i] = group_max(km[i], d.group_lanes);
-      vm[i] = group_max(vm[i], d.group_lanes);
-    }
+    for (int i = 0; i < kPasses; ++i) m[i] = group_max(m[i], d.group_lanes);
   }
 
   if (loc < 0 || loc >= p.size_limit) {
-    if (lane == 0) report_bad_token(token);
+    if (lane == 0 && !is_v) report_bad_token(token);
     return;
   }
   int64_t page, off;
@@ -573,33 +568,27 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
     page = loc / p.page_size;
     off = loc - page * p.page_size;
   }
-  const __amdgpu_buffer_rsrc_t kd =
-      row_rsrc(p.k_cache + page * p.kc_stride_page + off * p.kc_stride_offset);
-  const __amdgpu_buffer_rsrc_t vd =
-      row_rsrc(p.v_cache + page * p.vc_stride_page + off * p.vc_stride_offset);
-  uint8_t* kss = d.k_scales + page * d.ks_stride_page + off * d.ks_stride_offset;
-  uint8_t* vss = d.v_scales + page * d.vs_stride_page + off * d.vs_stride_offset;
+  const __amdgpu_buffer_rsrc_t dst = row_rsrc(t.cache + page * t.c_page + off * t.c_offset);
+  uint8_t* scales = is_v ? d.v_scales + page * d.vs_stride_page + off * d.vs_stride_offset
+                         : d.k_scales + page * d.ks_stride_page + off * d.ks_stride_offset;
+  const int64_t s_head = is_v ? d.vs_stride_head : d.ks_stride_head;
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
     const uint32_t u = i * kWave + lane;
     if (u < p.units) {
-      const float sk = dyn_scale(km[i]), sv = dyn_scale(vm[i]);
-      const float ik = 1.0f / sk, iv = 1.0f / sv;
-      // ik, iv are finite and non-zero unless a group holds an infinity
-      const bool k_ok = ik != 0.0f, v_ok = iv != 0.0f;
-      store16_sc1(kd, kdo[i], quantize16<kFp16, false>(ka[i], kb[i], ik, k_ok));
-      store16_sc1(vd, vdo[i], quantize16<kFp16, false>(va[i], vb[i], iv, v_ok));
+      const float sc = dyn_scale(m[i]);
+      const float inv = 1.0f / sc;
+      // inv is finite and non-zero unless the group holds an infinity
+      store16_sc1(dst, dof[i], quantize16<kFp16, false>(a[i], b[i], inv, inv != 0.0f));
       // One lane per group writes its scale: the first lane of each head
       // (per head, g < num_heads), or unit 0 alone (per token, g = 0).
       if (d.per_head ? (u & (d.group_lanes - 1)) == 0 : u == 0) {
         const uint32_t g = d.per_head ? u / d.group_lanes : 0u;
-        *reinterpret_cast<float*>(kss + g * d.ks_stride_head) = sk;
-        *reinterpret_cast<float*>(vss + g * d.vs_stride_head) = sv;
+        *reinterpret_cast<float*>(scales + g * s_head) = sc;
       }
     }
   }
 }
-
 // ---------------------------------------------------------------------------
 // Host side: validation, dispatch, launch.
 // ---------------------------------------------------------------------------
@@ -865,7 +854,8 @@ int fp8_paged_store(bool e5m2, const void* k, const void* v, void* k_cache, void
   const int passes = waves_units >= 2 ? 2 : 1;
   const int64_t slices = ceil_div(waves_units, passes);
   if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
-  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), (uint32_t)slices);
+  if (2 * slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
+  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), (uint32_t)(2 * slices));
   return passes == 2 ? launch_fp8_passes<2>(p, flat, fp16, i64, e5m2, grid, stream)
                      : launch_fp8_passes<1>(p, flat, fp16, i64, e5m2, grid, stream);
 }
@@ -1015,7 +1005,7 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
   const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
   const bool i64 = idx_dtype == KVSTORE_IDX_I64;
   const int64_t waves_units = ceil_div(d.base.units, kWave);
-  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock));
+  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), 2);
   if (waves_units <= 1) return launch_dyn_passes<1>(d, flat, fp16, i64, grid, stream);
   if (waves_units <= 2) return launch_dyn_passes<2>(d, flat, fp16, i64, grid, stream);
   return launch_dyn_passes<4>(d, flat, fp16, i64, grid, stream);
