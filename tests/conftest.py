@@ -1,3 +1,4 @@
+import importlib.util
 import os
 import sys
 
@@ -11,6 +12,18 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workloads")
+
+
+def pytest_sessionstart(session):
+    # Build the HIP library only when nothing is built (a fresh checkout):
+    # tests load what is built and never rebuild an existing library.
+    lib = os.path.join(ROOT, "fp8_kv_quantization_amd", "libkvstore.so")
+    if not os.path.exists(lib):
+        path = os.path.join(ROOT, "fp8_kv_quantization_amd", "_build.py")
+        spec = importlib.util.spec_from_file_location("_kvstore_build", path)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 def _gpu_present() -> bool:
