@@ -392,7 +392,9 @@ def bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh, n=100):
 
 def bench_decode(kv, torch, dev, kvgen, to_dev):
     """Decode copy (256 tokens, 2 KiB rows, int64, 2^20 slots): per-call time
-    back to back, single-call latency, both from HIP events."""
+    back to back, single-call latency, and per-call time when the calls are
+    replayed from a captured HIP graph (how a serving loop issues them), all
+    from HIP events."""
     c2 = kvgen.workload(2)
     S = 16
     sets = kvgen.disjoint_index_sets(c2, S)
@@ -405,10 +407,10 @@ def bench_decode(kv, torch, dev, kvgen, to_dev):
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    def call(s):
+    def call(s, on=None):
         st = kv.kvstore_copy(k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
                              idx[s].data_ptr(), kv.IDX_I64, 1, R, R, R, R, c2.num_tokens,
-                             c2.slots, sh)
+                             c2.slots, sh if on is None else on)
         if st:
             raise kv.KVStoreError(st, "kvstore_copy")
 
@@ -431,12 +433,30 @@ def bench_decode(kv, torch, dev, kvgen, to_dev):
         b.record(stream)
         b.synchronize()
         lat.append(a.elapsed_time(b) * 1e3)
+    # one graph holding S calls (one per index set), replayed back to back
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(S):
+            call(s, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = 25
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (reps * S)
+    del g
     st, _, _ = kv.kvstore_check_error(sh)
     assert st == kv.OK
     del kc, vc
     return {"workload": "decode copy (256 tok, 8x128 bf16, int64, 2^20 slots)",
             "us_per_call_back_to_back": round(b2b_us, 3),
             "us_single_call_median": round(statistics.median(lat), 3),
+            "us_per_call_graph_replay": round(graph_us, 3),
             "bytes": c2.algorithmic_bytes()}
 
 

@@ -399,58 +399,6 @@ def test_fp8_edge_scales_every_pattern(src, name):
 
 
 # ---------------------------------------------------------------------------
-# Store calls inside a captured HIP graph, replayed with eager work between
-# ---------------------------------------------------------------------------
-
-def test_graph_capture_replays_match_eager():
-    c3 = kvgen.workload(3, tokens=2000, slots=8192)
-    c4 = _fp8_case(tokens=700, pages=16)
-    k3, v3, i3 = to_dev(c3.k), to_dev(c3.v), to_dev(c3.indices)
-    k4, v4, i4 = to_dev(c4.k), to_dev(c4.v), to_dev(c4.indices)
-    ik = to_dev(np.array([c4.inv_k_bits], dtype=np.uint32).view(np.float32))
-    iv = to_dev(np.array([c4.inv_v_bits], dtype=np.uint32).view(np.float32))
-    R3, R4, D = c3.row_bytes, c4.row_elems, c4.head_dim
-    kc3 = sentinel_cache(c3.slots, R3)
-    vc3 = sentinel_cache(c3.slots, R3)
-    kc4 = sentinel_cache(c4.slots, R4)
-    vc4 = sentinel_cache(c4.slots, R4)
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-
-    def step(stream_handle):
-        st1 = kv.kvstore_copy(k3.data_ptr(), v3.data_ptr(), kc3.data_ptr(), vc3.data_ptr(),
-                              i3.data_ptr(), kv.IDX_I32, 1, R3, R3, R3, R3, c3.num_tokens,
-                              c3.slots, stream_handle)
-        st2 = kv.kvstore_fp8_paged(k4.data_ptr(), v4.data_ptr(), kc4.data_ptr(), vc4.data_ptr(),
-                                   i4.data_ptr(), kv.IDX_I32, 1, kv.SRC_BF16, c4.num_heads, D,
-                                   c4.in_stride_bytes, 2 * D, c4.in_stride_bytes, 2 * D,
-                                   64 * R4, R4, D, 64 * R4, R4, D, c4.num_tokens, c4.slots, 64,
-                                   ik.data_ptr(), iv.data_ptr(), stream_handle)
-        assert st1 == kv.OK and st2 == kv.OK
-
-    g = torch.cuda.CUDAGraph()
-    _say("graph capture")
-    with torch.cuda.stream(s):
-        g.capture_begin()
-        step(s.cuda_stream)
-        g.capture_end()
-    torch.cuda.synchronize()
-    okc3, ovc3, _ = oracle.run_case(c3)
-    okc4, ovc4, _ = oracle.run_case(c4)
-    for replay in range(3):
-        for t in (kc3, vc3, kc4, vc4):      # eager work between replays
-            t.fill_(0xFF)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        assert_cache_equal(kc3, okc3, f"replay {replay} k_cache (copy)")
-        assert_cache_equal(vc3, ovc3, f"replay {replay} v_cache (copy)")
-        assert_cache_equal(kc4, okc4, f"replay {replay} k_cache (fp8)")
-        assert_cache_equal(vc4, ovc4, f"replay {replay} v_cache (fp8)")
-    assert check_flag() == (kv.OK, -1, 0)
-
-
-# ---------------------------------------------------------------------------
 # Narrow alignment (8- and 4-byte lanes) and packed small rows
 # ---------------------------------------------------------------------------
 
