@@ -24,6 +24,16 @@ def pytest_sessionstart(session):
         mod = importlib.util.module_from_spec(spec)
         spec.loader.exec_module(mod)
         mod.build()
+    # The plain-C client of the ABI, likewise only when missing.
+    client = os.path.join(ROOT, "tests", "c_client", "kvstore_client")
+    if not os.path.exists(client):
+        import oracle
+        oracle.build()
+        path = os.path.join(ROOT, "tests", "c_client", "build_client.py")
+        spec = importlib.util.spec_from_file_location("_kvstore_client_build", path)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 def _gpu_present() -> bool:
