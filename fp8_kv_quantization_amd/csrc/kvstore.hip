@@ -31,6 +31,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kvstore.h"
 
 namespace {
@@ -598,8 +600,20 @@ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 constexpr int64_t kMaxGridY = 65535;
 
-int launch_status() {
-  return hipGetLastError() == hipSuccess ? KVSTORE_OK : KVSTORE_ERR_HIP;
+template <typename T> struct NoDeduce { typedef T type; };
+
+// Launches `kernel` through hipLaunchKernel and returns that launch's own
+// status, so an error left behind by an earlier, unrelated HIP call is
+// neither reported as ours nor cleared.  KVSTORE_ERR_HIP means the runtime
+// refused the launch (nothing ran).
+template <typename... Args>
+int launch(void (*kernel)(Args...), dim3 grid, dim3 block, uint32_t lds_bytes,
+           hipStream_t stream, typename NoDeduce<Args>::type... args) {
+  void* argv[] = {static_cast<void*>(&args)...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, argv, lds_bytes,
+                         stream) == hipSuccess
+             ? KVSTORE_OK
+             : KVSTORE_ERR_HIP;
 }
 
 // Resident copy blocks per CU: about 8 waves per CU.  The copy writes rows
@@ -611,19 +625,23 @@ constexpr int copy_blocks_per_cu(int chunks_per_wave) {
   return (chunks_per_wave == 1 ? 16 : 8) / kCopyWavesPerBlock;
 }
 
-// LDS bytes per CU of the current device (cached per device), 0 if unknown.
+// LDS bytes per CU of the current device (cached per device; calls from
+// several threads may fill an entry concurrently with the same value), 0 if
+// unknown.
 int64_t lds_per_cu() {
-  static int64_t cache[64];
+  static std::atomic<int64_t> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev] == 0) {
+  int64_t have = cache[dev].load(std::memory_order_relaxed);
+  if (have == 0) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
             hipSuccess || v <= 0)
       return 0;
-    cache[dev] = v;
+    have = v;
+    cache[dev].store(have, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return have;
 }
 
 template <int VW, typename IdxT>
@@ -637,9 +655,8 @@ int launch_copy_vw(const CopyParams& p, hipStream_t stream) {
     while ((int64_t(1) << shift) < lanes) ++shift;
     const int64_t rows_per_block = (int64_t)kPackWavesPerBlock * kPackRows * (kWave >> shift);
     const dim3 grid((uint32_t)ceil_div(p.batch, rows_per_block));
-    hipLaunchKernelGGL((kvstore_copy_packed_kernel<VW, IdxT>), grid,
-                       dim3(kWave * kPackWavesPerBlock), 0, stream, p, shift);
-    return launch_status();
+    return launch(kvstore_copy_packed_kernel<VW, IdxT>, grid, dim3(kWave * kPackWavesPerBlock), 0,
+                  stream, p, shift);
   }
   const int64_t chunks = ceil_div(p.row_bytes, kChunk);
   const int per_wave = (int)(chunks < kMaxChunksPerWave ? chunks : kMaxChunksPerWave);
@@ -651,12 +668,11 @@ int launch_copy_vw(const CopyParams& p, hipStream_t stream) {
   const int64_t lds = VW == 16 ? lds_per_cu() : 0;
   const uint32_t lds_bytes = lds > 0 ? (uint32_t)(lds / copy_blocks_per_cu(per_wave)) : 0;
   switch (per_wave) {
-    case 1: hipLaunchKernelGGL((kvstore_copy_kernel<VW, 1, IdxT>), grid, block, lds_bytes, stream, p); break;
-    case 2: hipLaunchKernelGGL((kvstore_copy_kernel<VW, 2, IdxT>), grid, block, lds_bytes, stream, p); break;
-    case 3: hipLaunchKernelGGL((kvstore_copy_kernel<VW, 3, IdxT>), grid, block, lds_bytes, stream, p); break;
-    default: hipLaunchKernelGGL((kvstore_copy_kernel<VW, 4, IdxT>), grid, block, lds_bytes, stream, p); break;
+    case 1: return launch(kvstore_copy_kernel<VW, 1, IdxT>, grid, block, lds_bytes, stream, p);
+    case 2: return launch(kvstore_copy_kernel<VW, 2, IdxT>, grid, block, lds_bytes, stream, p);
+    case 3: return launch(kvstore_copy_kernel<VW, 3, IdxT>, grid, block, lds_bytes, stream, p);
+    default: return launch(kvstore_copy_kernel<VW, 4, IdxT>, grid, block, lds_bytes, stream, p);
   }
-  return launch_status();
 }
 
 template <typename IdxT>
@@ -670,12 +686,10 @@ template <int kPasses, bool kFlat, bool kFp16, bool kE5M2>
 int launch_fp8_idx(const Fp8Params& p, bool i64, dim3 grid, hipStream_t stream) {
   const dim3 block(kBlockThreads);
   if (i64)
-    hipLaunchKernelGGL((kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, kE5M2, int64_t>), grid,
-                       block, 0, stream, p);
-  else
-    hipLaunchKernelGGL((kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, kE5M2, int32_t>), grid,
-                       block, 0, stream, p);
-  return launch_status();
+    return launch(kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, kE5M2, int64_t>, grid, block, 0,
+                  stream, p);
+  return launch(kvstore_fp8_paged_kernel<kPasses, kFlat, kFp16, kE5M2, int32_t>, grid, block, 0,
+                stream, p);
 }
 
 template <int kPasses, bool kE5M2>
@@ -699,12 +713,10 @@ template <int kPasses, bool kFlat, bool kFp16>
 int launch_dyn_idx(const Fp8DynParams& d, bool i64, dim3 grid, hipStream_t stream) {
   const dim3 block(kBlockThreads);
   if (i64)
-    hipLaunchKernelGGL((kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, int64_t>), grid, block,
-                       0, stream, d);
-  else
-    hipLaunchKernelGGL((kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, int32_t>), grid, block,
-                       0, stream, d);
-  return launch_status();
+    return launch(kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, int64_t>, grid, block, 0,
+                  stream, d);
+  return launch(kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, int32_t>, grid, block, 0,
+                stream, d);
 }
 
 template <int kPasses>

@@ -219,7 +219,11 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
  * index, KVSTORE_ERR_OOB when some did, KVSTORE_ERR_HIP on a runtime error.
  * first_bad_token (nullable) receives the smallest rejected token position of
  * any call since the last check, or -1; bad_count (nullable) the number of
- * rejected tokens.  This is the only call that synchronises.
+ * rejected tokens.  This is the only call that synchronises.  The flag is
+ * per device and shared by all streams: a store still running on another
+ * stream of the device while this call reads and clears the flag may have its
+ * report split between this check and the next, or lost, so check once no
+ * store is in flight on other streams.
  */
 int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* bad_count);
 

@@ -334,6 +334,31 @@ def test_empty_batch_touches_nothing():
     assert check_flag() == (kv.OK, -1, 0)
 
 
+def test_stale_runtime_error_is_not_reported_as_ours():
+    """A store's status is its own launch's: an error that an earlier,
+    unrelated HIP call left behind (here an invalid device ordinal, which the
+    runtime rejects on the host) does not fail the store."""
+    import ctypes
+    c = kvgen.workload(1, tokens=300, slots=1024)
+    k, v, idx = to_dev(c.k), to_dev(c.v), to_dev(c.indices)
+    kc = sentinel_cache(c.slots, c.row_bytes)
+    vc = sentinel_cache(c.slots, c.row_bytes)
+    torch.cuda.synchronize()
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    assert hip.hipSetDevice(1 << 20) != 0          # leaves an error behind
+    st = kv.kvstore_copy(k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                         idx.data_ptr(), kv.IDX_I32, 1, c.row_bytes, c.in_stride_bytes,
+                         c.in_stride_bytes, c.row_bytes, c.num_tokens, c.slots,
+                         torch.cuda.current_stream().cuda_stream)
+    hip.hipGetLastError()                          # clear it before any torch launch
+    assert st == kv.OK
+    okc, ovc, _ = oracle.run_case(c)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+    assert check_flag() == (kv.OK, -1, 0)
+
+
 def test_copy_largest_slot_of_the_prefill_cache():
     # 2^21 slots x 2 KiB: the last slot starts 4 GiB - 2 KiB into the cache,
     # beyond 32-bit offsets.
