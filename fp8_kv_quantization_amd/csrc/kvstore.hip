@@ -483,7 +483,8 @@ struct Fp8DynParams {
   int32_t per_head;
 };
 
-// max |x| over 16 source elements; NaN elements are ignored (fmaxf).
+// max |x| over 16 source elements; NaN elements are ignored (fmaxf), so the
+// result is a non-negative float that is never NaN.
 template <bool kFp16>
 __device__ __forceinline__ float amax16(u32x4 a, u32x4 b) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
@@ -501,10 +502,35 @@ __device__ __forceinline__ float amax16(u32x4 a, u32x4 b) {
   return m;
 }
 
-// Max over aligned groups of `lanes` lanes (a power of two <= 64).
-__device__ __forceinline__ float group_max(float v, uint32_t lanes) {
-  for (uint32_t m = 1; m < lanes; m <<= 1) v = __builtin_fmaxf(v, __shfl_xor(v, (int)m));
-  return v;
+// One DPP step of a lane max: each lane takes the larger of its value and the
+// value of the lane that the row permutation kCtrl selects.
+template <int kCtrl>
+__device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
+  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kCtrl, 0xF, 0xF, false);
+  return v > o ? v : o;
+}
+
+// Max over aligned groups of `lanes` lanes (a power of two <= 64), for
+// non-negative, non-NaN floats: their bit patterns order like their values, so
+// an unsigned max is exact.  Groups of up to 16 lanes reduce inside a DPP row
+// (quad swaps, then the half-row and row mirrors); a 32-lane group adds one
+// cross-row shuffle, and the whole wave combines its four rows with readlane.
+__device__ __forceinline__ float group_max(float x, uint32_t lanes) {
+  uint32_t v = __builtin_bit_cast(uint32_t, x);
+  if (lanes >= 2) v = dpp_max<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
+  if (lanes >= 4) v = dpp_max<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
+  if (lanes >= 8) v = dpp_max<0x141>(v);   // row_half_mirror: the other quad of 8
+  if (lanes >= 16) v = dpp_max<0x140>(v);  // row_mirror: the other 8 of the row
+  if (lanes == 64) {
+    const uint32_t r0 = __builtin_amdgcn_readlane(v, 0), r1 = __builtin_amdgcn_readlane(v, 16);
+    const uint32_t r2 = __builtin_amdgcn_readlane(v, 32), r3 = __builtin_amdgcn_readlane(v, 48);
+    const uint32_t lo = r0 > r1 ? r0 : r1, hi = r2 > r3 ? r2 : r3;
+    v = lo > hi ? lo : hi;
+  } else if (lanes == 32) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)v, 16);
+    v = v > o ? v : o;
+  }
+  return __builtin_bit_cast(float, v);
 }
 
 // fp32 scale of a group, at least the smallest normal float.
@@ -540,7 +566,7 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
       b[i] = load16(t.src, sof + 16u);
     }
   }
-  // Every lane takes part in the shuffles below, so the bounds check comes after.
+  // Every lane takes part in the lane reduction below, so the bounds check comes after.
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
     if (i * kWave + lane < p.units) m[i] = amax16<kFp16>(a[i], b[i]);

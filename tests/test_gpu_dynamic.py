@@ -94,7 +94,8 @@ def test_dynamic_full_size(per_head):
 @pytest.mark.parametrize("heads,dim,modes", [(1, 16, (False, True)), (3, 48, (False,)),
                                              (8, 64, (False, True)), (16, 128, (False, True)),
                                              (32, 128, (False, True)), (2, 576, (False,)),
-                                             (4, 1024, (False, True))])
+                                             (4, 1024, (False, True)), (2, 32, (True,)),
+                                             (4, 256, (False, True)), (8, 512, (False, True))])
 def test_dynamic_head_shapes(heads, dim, modes):
     rng = np.random.Generator(np.random.PCG64(heads * 7 + dim))
     T, P, pages = 150, 16, 12
