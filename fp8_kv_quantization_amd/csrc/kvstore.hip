@@ -124,7 +124,8 @@ struct CopyParams {
   int64_t cache_stride;
   int64_t size_limit;
   uint32_t row_bytes;
-  uint32_t batch;
+  uint32_t batch;       // tokens of this launch
+  uint32_t token_base;  // first token of this launch
 };
 
 // One row per wave.  Grid: x = ceil(batch / kCopyWavesPerBlock) blocks of
@@ -135,8 +136,9 @@ __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const C
   typedef typename LaneVec<VW>::type T;
   constexpr uint32_t kChunk = kWave * VW;
   const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t token = wave_uniform(blockIdx.x * kCopyWavesPerBlock + threadIdx.x / kWave);
-  if (token >= p.batch) return;
+  const uint32_t i = wave_uniform(blockIdx.x * kCopyWavesPerBlock + threadIdx.x / kWave);
+  if (i >= p.batch) return;
+  const uint32_t token = p.token_base + i;
   const uint32_t slice = blockIdx.y;
 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
@@ -192,21 +194,22 @@ __global__ __launch_bounds__(kWave * kPackWavesPerBlock) void kvstore_copy_packe
   int64_t loc[kPackRows];
 #pragma unroll
   for (int r = 0; r < kPackRows; ++r) {
-    const uint64_t t = ((uint64_t)wave * kPackRows + r) * rows_per_wave + (lane >> group_shift);
-    if (t < p.batch) {
-      loc[r] = load_index<IdxT>(p.indices, (int64_t)t * p.idx_stride);
+    const uint64_t i = ((uint64_t)wave * kPackRows + r) * rows_per_wave + (lane >> group_shift);
+    if (i < p.batch) {
+      const int64_t t = (int64_t)p.token_base + (int64_t)i;
+      loc[r] = load_index<IdxT>(p.indices, t * p.idx_stride);
       if (active) {
-        kr[r] = loadv<VW>(p.k + (int64_t)t * p.k_stride, col);
-        vr[r] = loadv<VW>(p.v + (int64_t)t * p.v_stride, col);
+        kr[r] = loadv<VW>(p.k + t * p.k_stride, col);
+        vr[r] = loadv<VW>(p.v + t * p.v_stride, col);
       }
     }
   }
 #pragma unroll
   for (int r = 0; r < kPackRows; ++r) {
-    const uint64_t t = ((uint64_t)wave * kPackRows + r) * rows_per_wave + (lane >> group_shift);
-    if (t >= p.batch) continue;
+    const uint64_t i = ((uint64_t)wave * kPackRows + r) * rows_per_wave + (lane >> group_shift);
+    if (i >= p.batch) continue;
     if (loc[r] < 0 || loc[r] >= p.size_limit) {
-      if (col == 0) report_bad_token((uint32_t)t);
+      if (col == 0) report_bad_token(p.token_base + (uint32_t)i);
       continue;
     }
     if (active) {
@@ -234,7 +237,8 @@ struct Fp8Params {
   int64_t vc_stride_page, vc_stride_offset, vc_stride_head;
   int64_t size_limit;
   int64_t page_size;
-  uint32_t batch;
+  uint32_t batch;           // tokens of this launch
+  uint32_t token_base;      // first token of this launch
   uint32_t units;           // 16-element units per row: num_heads * head_dim / 16
   uint32_t units_per_head;  // head_dim / 16
   int32_t page_shift;       // log2(page_size) when a power of two, else -1
@@ -430,8 +434,9 @@ __device__ __forceinline__ int64_t slot_offset(const Fp8Params& p, int64_t loc, 
 template <int kPasses, bool kFlat, bool kFp16, bool kE5M2, typename IdxT>
 __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const Fp8Params p) {
   const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
-  if (token >= p.batch) return;
+  const uint32_t i = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (i >= p.batch) return;
+  const uint32_t token = p.token_base + i;
   const bool is_v = (blockIdx.y & 1u) != 0;
   const uint32_t slice = blockIdx.y >> 1;
 
@@ -545,8 +550,9 @@ template <int kPasses, bool kFlat, bool kFp16, typename IdxT>
 __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(const Fp8DynParams d) {
   const Fp8Params& p = d.base;
   const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t token = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
-  if (token >= p.batch) return;
+  const uint32_t i = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
+  if (i >= p.batch) return;
+  const uint32_t token = p.token_base + i;
   const bool is_v = blockIdx.y != 0;
 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
@@ -649,6 +655,27 @@ int launch(void (*kernel)(Args...), dim3 grid, dim3 block, uint32_t lds_bytes,
 // bytes per wave, so they get twice the waves.
 constexpr int copy_blocks_per_cu(int chunks_per_wave) {
   return (chunks_per_wave == 1 ? 16 : 8) / kCopyWavesPerBlock;
+}
+
+// Tokens of one launch.  A grid with one wave per token then stays at 2^30
+// work-items, well inside the 2^32 limit of a dispatch dimension; larger
+// batches run as several launches on the same stream, in token order.
+constexpr uint32_t kMaxLaunchTokens = 1u << 24;
+
+// Calls fn(params) once per run of at most kMaxLaunchTokens tokens of
+// [0, batch), with token_base / count set to the run.  Stops at the first
+// status other than KVSTORE_OK.
+template <typename P, typename F>
+int launch_in_runs(P& params, uint32_t& token_base, uint32_t& count, uint32_t batch, F&& fn) {
+  for (uint32_t base = 0; base < batch;) {
+    const uint32_t n = batch - base < kMaxLaunchTokens ? batch - base : kMaxLaunchTokens;
+    token_base = base;
+    count = n;
+    const int st = fn(static_cast<const P&>(params));
+    if (st != KVSTORE_OK) return st;
+    base += n;
+  }
+  return KVSTORE_OK;
 }
 
 // LDS bytes per CU of the current device (cached per device; calls from
@@ -891,11 +918,12 @@ int fp8_paged_store(bool e5m2, const void* k, const void* v, void* k_cache, void
   const int64_t waves_units = ceil_div(p.units, kWave);
   const int passes = waves_units >= 2 ? 2 : 1;
   const int64_t slices = ceil_div(waves_units, passes);
-  if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
   if (2 * slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
-  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), (uint32_t)(2 * slices));
-  return passes == 2 ? launch_fp8_passes<2>(p, flat, fp16, i64, e5m2, grid, stream)
-                     : launch_fp8_passes<1>(p, flat, fp16, i64, e5m2, grid, stream);
+  return launch_in_runs(p, p.token_base, p.batch, batch, [&](const Fp8Params& run) {
+    const dim3 grid((uint32_t)ceil_div(run.batch, kWavesPerBlock), (uint32_t)(2 * slices));
+    return passes == 2 ? launch_fp8_passes<2>(run, flat, fp16, i64, e5m2, grid, stream)
+                       : launch_fp8_passes<1>(run, flat, fp16, i64, e5m2, grid, stream);
+  });
 }
 
 }  // namespace
@@ -936,9 +964,10 @@ int kvstore_copy(const void* k, const void* v, void* k_cache, void* v_cache,
   p.cache_stride = cache_stride_bytes;
   p.size_limit = size_limit;
   p.row_bytes = (uint32_t)row_bytes;
-  p.batch = batch;
-  return idx_dtype == KVSTORE_IDX_I64 ? launch_copy<int64_t>(p, vw, stream)
-                                      : launch_copy<int32_t>(p, vw, stream);
+  return launch_in_runs(p, p.token_base, p.batch, batch, [&](const CopyParams& run) {
+    return idx_dtype == KVSTORE_IDX_I64 ? launch_copy<int64_t>(run, vw, stream)
+                                        : launch_copy<int32_t>(run, vw, stream);
+  });
 }
 
 int kvstore_fp8_paged(const void* k, const void* v, void* k_cache, void* v_cache,
@@ -1043,10 +1072,12 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
   const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
   const bool i64 = idx_dtype == KVSTORE_IDX_I64;
   const int64_t waves_units = ceil_div(d.base.units, kWave);
-  const dim3 grid((uint32_t)ceil_div(batch, kWavesPerBlock), 2);
-  if (waves_units <= 1) return launch_dyn_passes<1>(d, flat, fp16, i64, grid, stream);
-  if (waves_units <= 2) return launch_dyn_passes<2>(d, flat, fp16, i64, grid, stream);
-  return launch_dyn_passes<4>(d, flat, fp16, i64, grid, stream);
+  return launch_in_runs(d, d.base.token_base, d.base.batch, batch, [&](const Fp8DynParams& run) {
+    const dim3 grid((uint32_t)ceil_div(run.base.batch, kWavesPerBlock), 2);
+    if (waves_units <= 1) return launch_dyn_passes<1>(run, flat, fp16, i64, grid, stream);
+    if (waves_units <= 2) return launch_dyn_passes<2>(run, flat, fp16, i64, grid, stream);
+    return launch_dyn_passes<4>(run, flat, fp16, i64, grid, stream);
+  });
 }
 
 int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* bad_count) {

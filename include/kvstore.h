@@ -70,7 +70,9 @@ enum { KVSTORE_SRC_BF16 = 0, KVSTORE_SRC_FP16 = 1 };
 enum { KVSTORE_SCALE_PER_TOKEN = 0, KVSTORE_SCALE_PER_TOKEN_HEAD = 1 };
 
 /* Status codes.  Negative codes returned by a store call mean nothing was
- * launched and no memory was touched. */
+ * launched and no memory was touched, with one exception: a batch above 2^24
+ * tokens runs as several launches (see `batch` below), and KVSTORE_ERR_HIP
+ * from a later launch leaves the earlier runs queued. */
 enum {
   KVSTORE_OK = 0,
   KVSTORE_ERR_NULL = -1,  /* a required pointer is NULL */
@@ -96,6 +98,10 @@ enum {
  *   *_stride_bytes  multiples of 4; k/v strides >= 0,
  *                cache_stride_bytes >= row_bytes.
  *   batch        number of tokens; 0 returns KVSTORE_OK and launches nothing.
+ *                Above 2^24 tokens the call queues one launch per run of at
+ *                most 2^24 tokens, in token order, on `stream` (the grid of
+ *                one launch stays far below 2^32 work-items); token positions
+ *                in the flag stay those of the whole batch.
  *   size_limit   valid slots are [0, size_limit); > 0, and
  *                size_limit * cache_stride_bytes must fit in int64.
  *   stream       HIP stream of the current device (0 = null stream).
