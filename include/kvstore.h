@@ -94,7 +94,10 @@ enum {
  *   indices      device, element t at indices[t * idx_stride], of type
  *                idx_dtype (KVSTORE_IDX_I32 / KVSTORE_IDX_I64).
  *   idx_stride   in elements, >= 1.
- *   row_bytes    bytes per K (and V) row: > 0, a multiple of 4, < 2^31.
+ *   row_bytes    bytes per K (and V) row: > 0, a multiple of 4, < 2^31, and
+ *                at most 65535 * 4 * 64 lane vectors (268,431,360 bytes with
+ *                16-byte lanes, 134,215,680 with 8-byte, 67,107,840 with
+ *                4-byte lanes; longer rows return KVSTORE_ERR_SHAPE).
  *   *_stride_bytes  multiples of 4; k/v strides >= 0,
  *                cache_stride_bytes >= row_bytes.
  *   batch        number of tokens; 0 returns KVSTORE_OK and launches nothing.
@@ -136,7 +139,10 @@ int kvstore_copy(const void* k, const void* v, void* k_cache, void* v_cache,
  *                this way.
  *   indices, idx_dtype, idx_stride, batch, size_limit, stream: as in
  *                kvstore_copy; size_limit is normally num_pages * page_size.
- *   num_heads    > 0;  head_dim > 0 and a multiple of 16.
+ *   num_heads    > 0;  head_dim > 0 and a multiple of 16;  num_heads *
+ *                head_dim <= 67,106,816 elements, and the byte offset of the
+ *                last head's end within a token row or a slot below 2^31
+ *                (else KVSTORE_ERR_SHAPE).
  *   page_size    > 0 (any value; powers of two take a shift).
  *   inv_k_scale_ptr, inv_v_scale_ptr
  *                device pointers to one fp32 inverse scale each, or NULL for

@@ -71,6 +71,22 @@ COPY_OK = dict(k=A, v=A + 0x100000, k_cache=A + 0x200000, v_cache=A + 0x300000,
                k_stride_bytes=2048, v_stride_bytes=2048, cache_stride_bytes=2048, batch=16,
                size_limit=1024)
 
+# Longest row per lane width: 65535 grid slices x 4 chunks x 64 lanes x VW bytes.
+COPY_MAX_ROW = {vw: 65535 * 4 * 64 * vw for vw in (16, 8, 4)}
+# Most elements per FP8 row: 2 x 65535 grid rows (K and V) hold 32767 slices of
+# 2 waves' worth of 16-element units each.
+FP8_MAX_ELEMS = 32767 * 2 * 64 * 16
+
+
+def _fp8_wide(elems):
+    """A one-head FP8 layout with `elems` elements per row (flat caches)."""
+    return dict(num_heads=1, head_dim=elems, k_stride_token_bytes=2 * elems,
+                v_stride_token_bytes=2 * elems, k_stride_head_bytes=0, v_stride_head_bytes=0,
+                kc_stride_page_bytes=64 * elems, kc_stride_offset_bytes=elems,
+                kc_stride_head_bytes=0, vc_stride_page_bytes=64 * elems,
+                vc_stride_offset_bytes=elems, vc_stride_head_bytes=0)
+
+
 COPY_BAD = [
     ("null_k", dict(k=0), -1),
     ("null_cache", dict(v_cache=0), -1),
@@ -82,6 +98,13 @@ COPY_BAD = [
     ("row_too_big", dict(row_bytes=1 << 31, cache_stride_bytes=1 << 31, k_stride_bytes=0,
                          v_stride_bytes=0), -2),
     ("cache_stride_below_row", dict(cache_stride_bytes=1024), -2),
+    # rows over 65535 grid slices of 4 lane-vector chunks
+    ("row_over_slices_16B_lanes", dict(row_bytes=COPY_MAX_ROW[16] + 16, k_stride_bytes=0,
+                                       v_stride_bytes=0,
+                                       cache_stride_bytes=COPY_MAX_ROW[16] + 16), -2),
+    ("row_over_slices_4B_lanes", dict(row_bytes=COPY_MAX_ROW[4] + 4, k_stride_bytes=0,
+                                      v_stride_bytes=0,
+                                      cache_stride_bytes=COPY_MAX_ROW[4] + 4), -2),
     ("negative_k_stride", dict(k_stride_bytes=-2048), -2),
     ("size_limit_zero", dict(size_limit=0), -2),
     ("size_limit_overflow", dict(size_limit=1 << 62), -2),
@@ -120,6 +143,7 @@ FP8_BAD = [
     ("scale_misaligned", dict(inv_k_scale_ptr=A + 2), -3),
     ("cache_misaligned", dict(v_cache=A + 8), -3),
     ("idx_stride_zero", dict(idx_stride=0), -2),
+    ("row_over_slices", _fp8_wide(FP8_MAX_ELEMS + 16), -2),
 ]
 
 
@@ -175,6 +199,12 @@ def test_valid_arguments_reach_the_runtime(kv):
     assert _fp8_call(kv, _entry=kv.kvstore_fp8_paged_e5m2) == kv.ERR_HIP
     # 8- and 4-byte aligned rows and pointers are accepted by the copy
     assert _copy_call(kv, row_bytes=2040, k=A + 8) == kv.ERR_HIP
+    # the longest rows pass validation
+    # (a row of 4 mod 16 bytes takes 4-byte lanes)
+    for row in (COPY_MAX_ROW[16], COPY_MAX_ROW[4] - 12):
+        assert _copy_call(kv, row_bytes=row, k_stride_bytes=0, v_stride_bytes=0,
+                          cache_stride_bytes=row) == kv.ERR_HIP
+    assert _fp8_call(kv, **_fp8_wide(FP8_MAX_ELEMS)) == kv.ERR_HIP
     assert _copy_call(kv, row_bytes=36, k_stride_bytes=36, v_stride_bytes=40,
                       cache_stride_bytes=36, v_cache=A + 0x300004) == kv.ERR_HIP
 
