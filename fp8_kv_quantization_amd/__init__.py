@@ -177,9 +177,9 @@ def _torch():
     return torch
 
 
-def _stream_handle(stream):
+def _stream_handle(stream, device=None):
     torch = _torch()
-    s = torch.cuda.current_stream() if stream is None else stream
+    s = torch.cuda.current_stream(device) if stream is None else stream
     return s.cuda_stream
 
 
@@ -192,15 +192,35 @@ def _idx_code(indices) -> int:
     raise TypeError(f"indices must be int32 or int64, got {indices.dtype}")
 
 
-def _check_cuda(*tensors):
+def _device_of(*tensors):
+    """The one GPU that holds every tensor (the store runs there)."""
+    dev = None
     for t in tensors:
+        if t is None:
+            continue
         if not t.is_cuda:
             raise ValueError("all tensors must be on the GPU")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"all tensors must be on one GPU (found {dev} and {t.device})")
+    return dev
+
+
+def _size_limit(size_limit, slots):
+    """size_limit, defaulting to the cache's slot count and never beyond it
+    (the kernels bound indices by it, so a larger value could write past the
+    cache tensor)."""
+    limit = slots if size_limit is None else int(size_limit)
+    if limit > slots:
+        raise ValueError(f"size_limit ({limit}) exceeds the cache's {slots} slots")
+    return limit
 
 
 def store_kv(k, v, k_cache, v_cache, indices, size_limit=None, stream=None) -> None:
     """Scatter copy: k_cache[indices[t]] = k[t], v_cache[indices[t]] = v[t]."""
-    _check_cuda(k, v, k_cache, v_cache, indices)
+    torch = _torch()
+    dev = _device_of(k, v, k_cache, v_cache, indices)
     if k.dim() != 2 or v.dim() != 2 or k_cache.dim() != 2 or v_cache.dim() != 2:
         raise ValueError("k, v, k_cache, v_cache must be 2-D")
     if indices.dim() != 1 or indices.shape[0] != k.shape[0] or v.shape[0] != k.shape[0]:
@@ -217,11 +237,13 @@ def store_kv(k, v, k_cache, v_cache, indices, size_limit=None, stream=None) -> N
     if k_cache.shape[0] != v_cache.shape[0]:
         raise ValueError("k_cache and v_cache must have the same number of slots")
     es = k.element_size()
-    limit = k_cache.shape[0] if size_limit is None else int(size_limit)
-    st = kvstore_copy(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-                      indices.data_ptr(), _idx_code(indices), indices.stride(0) if k.shape[0] else 1,
-                      D * es, k.stride(0) * es, v.stride(0) * es, k_cache.stride(0) * es,
-                      k.shape[0], limit, _stream_handle(stream))
+    limit = _size_limit(size_limit, k_cache.shape[0])
+    with torch.cuda.device(dev):
+        st = kvstore_copy(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                          indices.data_ptr(), _idx_code(indices),
+                          indices.stride(0) if k.shape[0] else 1, D * es, k.stride(0) * es,
+                          v.stride(0) * es, k_cache.stride(0) * es, k.shape[0], limit,
+                          _stream_handle(stream, dev))
     if st != OK:
         raise KVStoreError(st, "kvstore_copy")
 
@@ -277,7 +299,7 @@ def store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16, inv_k_sc
     if fp8_format not in ("e4m3fn", "e5m2"):
         raise ValueError(f"unknown fp8_format {fp8_format!r}")
     entry = kvstore_fp8_paged_e5m2 if fp8_format == "e5m2" else kvstore_fp8_paged
-    _check_cuda(k, v, k_cache, v_cache, cache_loc)
+    dev = _device_of(k, v, k_cache, v_cache, cache_loc, inv_k_scale, inv_v_scale)
     if k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16:
         src = SRC_BF16
     elif k.dtype == torch.float16 and v.dtype == torch.float16:
@@ -301,11 +323,12 @@ def store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16, inv_k_sc
         if s.dtype != torch.float32 or s.numel() != 1 or not s.is_cuda:
             raise TypeError("inverse scales must be one-element fp32 GPU tensors")
         ptrs.append(s.data_ptr())
-    limit = slots if size_limit is None else int(size_limit)
-    st = entry(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
-               cache_loc.data_ptr(), _idx_code(cache_loc), cache_loc.stride(0) if T else 1, src,
-               H, D, ks[0], ks[1], vs[0], vs[1], kcs[0], kcs[1], kcs[2], vcs[0], vcs[1], vcs[2],
-               T, limit, page_size, ptrs[0], ptrs[1], _stream_handle(stream))
+    limit = _size_limit(size_limit, slots)
+    with torch.cuda.device(dev):
+        st = entry(k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                   cache_loc.data_ptr(), _idx_code(cache_loc), cache_loc.stride(0) if T else 1,
+                   src, H, D, ks[0], ks[1], vs[0], vs[1], kcs[0], kcs[1], kcs[2], vcs[0], vcs[1],
+                   vcs[2], T, limit, page_size, ptrs[0], ptrs[1], _stream_handle(stream, dev))
     if st != OK:
         raise KVStoreError(st, entry.__name__)
 
@@ -335,7 +358,7 @@ def store_kv_fp8_paged_dynamic(k, v, k_cache, v_cache, cache_loc, k_scale_cache,
     """Fused e4m3fn quantise + paged store with per-token (or per token and
     head) scales computed in the kernel and written to the scale caches."""
     torch = _torch()
-    _check_cuda(k, v, k_cache, v_cache, cache_loc, k_scale_cache, v_scale_cache)
+    dev = _device_of(k, v, k_cache, v_cache, cache_loc, k_scale_cache, v_scale_cache)
     if k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16:
         src = SRC_BF16
     elif k.dtype == torch.float16 and v.dtype == torch.float16:
@@ -355,22 +378,27 @@ def store_kv_fp8_paged_dynamic(k, v, k_cache, v_cache, cache_loc, k_scale_cache,
     T = k.shape[0]
     if v.shape[0] != T or cache_loc.dim() != 1 or cache_loc.shape[0] != T:
         raise ValueError("cache_loc must be [T] with T = k.shape[0] = v.shape[0]")
-    limit = slots if size_limit is None else int(size_limit)
-    st = kvstore_fp8_paged_dynamic(
-        k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), cache_loc.data_ptr(),
-        _idx_code(cache_loc), cache_loc.stride(0) if T else 1, src, H, D, ks[0], ks[1], vs[0],
-        vs[1], kcs[0], kcs[1], kcs[2], vcs[0], vcs[1], vcs[2], k_scale_cache.data_ptr(),
-        v_scale_cache.data_ptr(), SCALE_PER_TOKEN_HEAD if per_head else SCALE_PER_TOKEN,
-        kss[0], kss[1], kss[2], vss[0], vss[1], vss[2], T, limit, page_size,
-        _stream_handle(stream))
+    limit = _size_limit(size_limit, slots)
+    with torch.cuda.device(dev):
+        st = kvstore_fp8_paged_dynamic(
+            k.data_ptr(), v.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            cache_loc.data_ptr(), _idx_code(cache_loc), cache_loc.stride(0) if T else 1, src, H,
+            D, ks[0], ks[1], vs[0], vs[1], kcs[0], kcs[1], kcs[2], vcs[0], vcs[1], vcs[2],
+            k_scale_cache.data_ptr(), v_scale_cache.data_ptr(),
+            SCALE_PER_TOKEN_HEAD if per_head else SCALE_PER_TOKEN, kss[0], kss[1], kss[2],
+            vss[0], vss[1], vss[2], T, limit, page_size, _stream_handle(stream, dev))
     if st != OK:
         raise KVStoreError(st, "kvstore_fp8_paged_dynamic")
 
 
-def check_error(stream=None):
-    """(first_bad_token, bad_count) since the last check; (-1, 0) if none.
-    Synchronises the stream."""
-    st, fb, bc = kvstore_check_error(_stream_handle(stream))
+def check_error(stream=None, device=None):
+    """(first_bad_token, bad_count) since the last check on `device` (default:
+    the current device); (-1, 0) if none.  Synchronises the stream (default:
+    that device's current stream)."""
+    torch = _torch()
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    with torch.cuda.device(dev):
+        st, fb, bc = kvstore_check_error(_stream_handle(stream, dev))
     if st not in (OK, ERR_OOB):
         raise KVStoreError(st, "kvstore_check_error")
     return fb, bc

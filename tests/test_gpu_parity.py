@@ -399,6 +399,36 @@ def test_store_kv_tensor_api():
     np.testing.assert_array_equal(vc.view(torch.uint8).cpu().numpy(), ovc)
 
 
+def test_tensor_api_rejects_size_limit_beyond_the_cache():
+    """The tensor-level calls refuse a size_limit above the cache's slots
+    (the kernels bound indices by it), before anything is launched."""
+    c = kvgen.workload(1, tokens=50, slots=256)
+    k, v, idx = to_dev(c.k), to_dev(c.v), to_dev(c.indices)
+    kc = sentinel_cache(c.slots, c.row_bytes)
+    vc = sentinel_cache(c.slots, c.row_bytes)
+    with pytest.raises(ValueError, match="size_limit"):
+        kv.store_kv(k.view(torch.uint8), v.view(torch.uint8), kc, vc, idx, size_limit=c.slots + 1)
+    f = _fp8_case(tokens=40, pages=2)
+    H, D, P = f.num_heads, f.head_dim, f.page_size
+    fk = to_dev(f.k).view(torch.bfloat16).view(-1, H, D)
+    fv = to_dev(f.v).view(torch.bfloat16).view(-1, H, D)
+    fkc = sentinel_cache(f.slots, f.row_elems).view(-1, P, H, D)
+    fvc = sentinel_cache(f.slots, f.row_elems).view(-1, P, H, D)
+    fidx = to_dev(f.indices)
+    with pytest.raises(ValueError, match="size_limit"):
+        kv.store_kv_fp8_paged(fk, fv, fkc, fvc, fidx, page_size=P, size_limit=f.slots + 1)
+    ks = torch.zeros((f.slots,), dtype=torch.float32, device=DEV)
+    vs = torch.zeros_like(ks)
+    with pytest.raises(ValueError, match="size_limit"):
+        kv.store_kv_fp8_paged_dynamic(fk, fv, fkc, fvc, fidx, ks, vs, page_size=P,
+                                      size_limit=f.slots + 1)
+    torch.cuda.synchronize()
+    for t in (kc, vc, fkc, fvc):
+        assert bool((t == 0xFF).all())
+    assert bool((ks == 0).all())
+    assert kv.check_error() == (-1, 0)
+
+
 # ---------------------------------------------------------------------------
 # Edge-case inverse scales (exact path: zero, infinite, NaN; fast path:
 # negative, denormal, huge) on every input pattern
