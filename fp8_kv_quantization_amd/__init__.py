@@ -199,7 +199,7 @@ def _device_of(*tensors):
         if t is None:
             continue
         if not t.is_cuda:
-            raise ValueError("all tensors must be on the GPU")
+            raise ValueError("every tensor must be a GPU tensor")
         if dev is None:
             dev = t.device
         elif t.device != dev:
@@ -256,18 +256,18 @@ def _cache_strides(cache, page_size):
     if cache.dim() == 3:
         slots, H, D = cache.shape
         if slots % page_size:
-            raise ValueError(f"total_slots ({slots}) must be divisible by page_size ({page_size})")
+            raise ValueError(f"a flat cache of {slots} slots does not split into pages of {page_size}")
         if cache.stride(2) != 1:
             raise ValueError("cache dim stride must be 1")
         return H, D, slots, (cache.stride(0) * page_size, cache.stride(0), cache.stride(1))
     if cache.dim() == 4:
         pages, ps, H, D = cache.shape
         if ps != page_size:
-            raise ValueError(f"page_size mismatch: cache has {ps}, expected {page_size}")
+            raise ValueError(f"the paged cache holds {ps} slots per page, not page_size={page_size}")
         if cache.stride(3) != 1:
             raise ValueError("cache dim stride must be 1")
         return H, D, pages * ps, (cache.stride(0), cache.stride(1), cache.stride(2))
-    raise ValueError(f"Unsupported cache ndim={cache.dim()}, expected 3 or 4")
+    raise ValueError(f"a cache is 3-D (flat) or 4-D (paged), not {cache.dim()}-D")
 
 
 def _input_strides(x, H, D):
@@ -285,7 +285,7 @@ def _input_strides(x, H, D):
         if x.stride(1) != 1:
             raise ValueError("input dim stride must be 1")
         return x.stride(0) * es, D * es
-    raise ValueError(f"Unsupported input ndim={x.dim()}, expected 2 or 3")
+    raise ValueError(f"k and v are 2-D [T, H*D] or 3-D [T, H, D], not {x.dim()}-D")
 
 
 def store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16, inv_k_scale=None,

@@ -25,9 +25,10 @@
  *   kvstore_fp8_paged_e5m2 -- the same store into float8_e5m2 caches, which
  *                         the page's unfused path also writes.
  *   kvstore_fp8_paged_dynamic -- the same store with per-token (or per token
- *                         and head) scales computed in the kernel, the step
- *                         the docstring of "trtllm_fp8_kv_kernel.py" lists as
- *                         "per-token or per-page scale computation".
+ *                         and head) scales computed in the kernel: the module
+ *                         docstring of "trtllm_fp8_kv_kernel.py" counts scale
+ *                         computation (per token, and per page) among the
+ *                         fused kernel's steps.
  *
  * Numerics of kvstore_fp8_paged: x (bf16 or fp16) is widened to fp32 exactly,
  * multiplied once in fp32 (round to nearest) by the inverse scale, and
