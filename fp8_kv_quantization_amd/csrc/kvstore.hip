@@ -374,6 +374,29 @@ __device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv, bool sc
   return out;
 }
 
+// Byte offsets of 8-element group g inside one token's source row (16 bytes
+// per group) and inside one cache slot (8 bytes per group).  kFlat: heads are
+// back to back in both (offsets linear in g).
+template <bool kFlat>
+__device__ __forceinline__ void group_offsets(uint32_t g, uint32_t groups_per_head,
+                                              int64_t src_head, int64_t dst_head,
+                                              uint32_t* src_off, uint32_t* dst_off) {
+  if constexpr (kFlat) {
+    *src_off = g * 16u;
+    *dst_off = g * 8u;
+  } else {
+    const uint32_t h = g / groups_per_head;
+    const uint32_t r = g - h * groups_per_head;
+    *src_off = (uint32_t)(h * src_head) + r * 16u;
+    *dst_off = (uint32_t)(h * dst_head) + r * 8u;
+  }
+}
+
+// 8-byte store with the sc1 cache policy.
+__device__ __forceinline__ void store8_sc1(__amdgpu_buffer_rsrc_t row, uint32_t off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, row, (int)off, 0, 16);
+}
+
 // Byte offsets of 16-element unit u inside one token's source row and inside
 // one cache slot.  kFlat: heads are back to back in both (offsets linear in u).
 template <bool kFlat>
@@ -447,16 +470,26 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
   // product can be NaN: finite, non-zero scale and no NaN input.
   const bool scale_ok = __builtin_fabsf(inv) <= 3.40282347e38f && inv != 0.0f;
 
+  // Each pass covers 128 groups of 8 elements (1024 elements): lane l takes
+  // groups l and l + 64, so each load instruction of the wave reads 1 KiB of
+  // consecutive groups and each store writes 512 bytes of them.
+  const uint32_t groups = 2u * p.units;
+  const uint32_t groups_per_head = 2u * p.units_per_head;
   u32x4 a[kPasses], b[kPasses];
-  uint32_t dof[kPasses];
+  uint32_t da[kPasses], db[kPasses];
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
-    const uint32_t u = (slice * kPasses + i) * kWave + lane;
-    if (u < p.units) {
-      uint32_t sof;
-      unit_offsets<kFlat>(u, p.units_per_head, t.src_head, t.c_head, &sof, &dof[i]);
-      a[i] = load16(t.src, sof);
-      b[i] = load16(t.src, sof + 16u);
+    const uint32_t g = (slice * kPasses + i) * (2u * kWave) + lane;
+    a[i] = u32x4{0u, 0u, 0u, 0u};
+    b[i] = u32x4{0u, 0u, 0u, 0u};
+    uint32_t so;
+    if (g < groups) {
+      group_offsets<kFlat>(g, groups_per_head, t.src_head, t.c_head, &so, &da[i]);
+      a[i] = load16(t.src, so);
+    }
+    if (g + kWave < groups) {
+      group_offsets<kFlat>(g + kWave, groups_per_head, t.src_head, t.c_head, &so, &db[i]);
+      b[i] = load16(t.src, so);
     }
   }
 
@@ -467,8 +500,13 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
   const __amdgpu_buffer_rsrc_t d = row_rsrc(t.cache + slot_offset(p, loc, t.c_page, t.c_offset));
 #pragma unroll
   for (int i = 0; i < kPasses; ++i) {
-    const uint32_t u = (slice * kPasses + i) * kWave + lane;
-    if (u < p.units) store16_sc1(d, dof[i], quantize16<kFp16, kE5M2>(a[i], b[i], inv, scale_ok));
+    const uint32_t g = (slice * kPasses + i) * (2u * kWave) + lane;
+    if (g < groups) {
+      // bytes 0-7 of q come from group g (a), bytes 8-15 from group g + 64 (b)
+      const u32x4 q = quantize16<kFp16, kE5M2>(a[i], b[i], inv, scale_ok);
+      store8_sc1(d, da[i], u32x2{q.x, q.y});
+      if (g + kWave < groups) store8_sc1(d, db[i], u32x2{q.z, q.w});
+    }
   }
 }
 
