@@ -6,14 +6,17 @@
 //   * kvstore_fp8_paged -- bf16/fp16 -> e4m3fn quantise fused with the paged
 //                          [page, offset, head, dim] write
 //                          (sglang "trtllm_fp8_kv_kernel.py",
-//                          _fused_fp8_set_kv_buffer_kernel).
+//                          _fused_fp8_set_kv_buffer_kernel); also into e5m2
+//                          caches, and with scales computed per token or per
+//                          token and head (kvstore_fp8_paged_e5m2 / _dynamic).
 //
 // Both are pure data movement, bound by HBM bandwidth; no MFMA and no LDS.
 // Design points for CDNA4:
-//   * one 64-lane wave per (token, slice of the row); each lane moves 16 B per
-//     access (dwordx4), so one wave access covers 1 KiB of a row; rows or
-//     pointers aligned only to 8 or 4 bytes use 8- or 4-byte lanes, and rows
-//     that need at most 32 lanes are packed several to a wave;
+//   * one 64-lane wave per (token, slice of the row) -- for fp8, per (token,
+//     K or V); each lane loads 16 B per access (dwordx4), so one wave access
+//     covers 1 KiB of consecutive row bytes; copy rows or pointers aligned
+//     only to 8 or 4 bytes use 8- or 4-byte lanes, and copy rows that need at
+//     most 32 lanes are packed several to a wave;
 //   * every load of a wave (K and V, all its 1 KiB chunks) is issued before the
 //     index is needed: the source address does not depend on the index, so the
 //     index fetch overlaps the data fetch instead of preceding it;
@@ -40,8 +43,6 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;                     // lanes per wavefront (CDNA)
-constexpr int kLaneBytes = 16;                // bytes per lane per access
-constexpr int kChunkBytes = kWave * kLaneBytes;  // 1 KiB per wave access
 constexpr int kWavesPerBlock = 2;             // fp8 kernels
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kCopyWavesPerBlock = 2;         // copy kernel
@@ -95,19 +96,11 @@ __device__ __forceinline__ u32x4 load16(const uint8_t* base, uint32_t off) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
 }
 
-__device__ __forceinline__ void store16(uint8_t* base, uint32_t off, u32x4 v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(base + off));
-}
-
 // Raw buffer descriptor over [row, row + 2^31): stride 0, CDNA data format word.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(uint8_t* row) {
   return __builtin_amdgcn_make_buffer_rsrc(row, 0, 0x7FFFFFFF, 0x00020000);
 }
 
-// 16-byte store with the sc1 cache policy (bit 4 of the buffer cache-policy operand).
-__device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t row, uint32_t off, u32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, row, (int)off, 0, 16);
-}
 
 // ---------------------------------------------------------------------------
 // Scatter copy.
@@ -325,16 +318,17 @@ __device__ __forceinline__ bool any_nan16(u32x4 a, u32x4 b) {
   return (acc & 0x80008000u) != 0;
 }
 
-// Same result as quantize16 when no product can be NaN (no NaN input, scale
+// Same result as quantize16 when no product can be NaN (no NaN input, scales
 // finite and non-zero): the clamp is one v_med3_f32 and no NaN fix-up is needed.
 template <bool kFp16, bool kE5M2>
-__device__ __forceinline__ u32x4 quantize16_no_nan(u32x4 a, u32x4 b, float inv) {
+__device__ __forceinline__ u32x4 quantize16_no_nan(u32x4 a, u32x4 b, float inv_a, float inv_b) {
   constexpr float M = fp8_max<kE5M2>();
   u32x4 out;
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t w0 = w[2 * i], w1 = w[2 * i + 1];
+    const float inv = i < 2 ? inv_a : inv_b;
     float e0, e1, e2, e3;
     if constexpr (kFp16) {
       e0 = f16_lo(w0); e1 = f16_hi(w0); e2 = f16_lo(w1); e3 = f16_hi(w1);
@@ -352,16 +346,20 @@ __device__ __forceinline__ u32x4 quantize16_no_nan(u32x4 a, u32x4 b, float inv) 
   return out;
 }
 
-// 16 source elements (two 16-byte vectors) -> 16 FP8 bytes.  scale_ok: the
-// inverse scale is finite and non-zero (wave-uniform).
+// 16 source elements (two 16-byte vectors) -> 16 FP8 bytes: the 8 elements
+// of a scaled by inv_a give bytes 0-7, the 8 of b scaled by inv_b bytes 8-15.
+// scale_ok: both inverse scales are finite and non-zero.
 template <bool kFp16, bool kE5M2>
-__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv, bool scale_ok) {
-  if (scale_ok && !any_nan16<kFp16>(a, b)) return quantize16_no_nan<kFp16, kE5M2>(a, b, inv);
+__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv_a, float inv_b,
+                                            bool scale_ok) {
+  if (scale_ok && !any_nan16<kFp16>(a, b))
+    return quantize16_no_nan<kFp16, kE5M2>(a, b, inv_a, inv_b);
   u32x4 out;
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t w0 = w[2 * i], w1 = w[2 * i + 1];
+    const float inv = i < 2 ? inv_a : inv_b;
     float e0, e1, e2, e3;
     if constexpr (kFp16) {
       e0 = f16_lo(w0); e1 = f16_hi(w0); e2 = f16_lo(w1); e3 = f16_hi(w1);
@@ -392,26 +390,9 @@ __device__ __forceinline__ void group_offsets(uint32_t g, uint32_t groups_per_he
   }
 }
 
-// 8-byte store with the sc1 cache policy.
+// 8-byte store with the sc1 cache policy (bit 4 of the buffer cache-policy operand).
 __device__ __forceinline__ void store8_sc1(__amdgpu_buffer_rsrc_t row, uint32_t off, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, row, (int)off, 0, 16);
-}
-
-// Byte offsets of 16-element unit u inside one token's source row and inside
-// one cache slot.  kFlat: heads are back to back in both (offsets linear in u).
-template <bool kFlat>
-__device__ __forceinline__ void unit_offsets(uint32_t u, uint32_t units_per_head,
-                                             int64_t src_head, int64_t dst_head,
-                                             uint32_t* src_off, uint32_t* dst_off) {
-  if constexpr (kFlat) {
-    *src_off = u * 32u;
-    *dst_off = u * 16u;
-  } else {
-    const uint32_t h = u / units_per_head;
-    const uint32_t d = u - h * units_per_head;
-    *src_off = (uint32_t)(h * src_head) + d * 32u;
-    *dst_off = (uint32_t)(h * dst_head) + d * 16u;
-  }
 }
 
 // One tensor (K or V) of one token, as the wave sees it.
@@ -503,7 +484,7 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
     const uint32_t g = (slice * kPasses + i) * (2u * kWave) + lane;
     if (g < groups) {
       // bytes 0-7 of q come from group g (a), bytes 8-15 from group g + 64 (b)
-      const u32x4 q = quantize16<kFp16, kE5M2>(a[i], b[i], inv, scale_ok);
+      const u32x4 q = quantize16<kFp16, kE5M2>(a[i], b[i], inv, inv, scale_ok);
       store8_sc1(d, da[i], u32x2{q.x, q.y});
       if (g + kWave < groups) store8_sc1(d, db[i], u32x2{q.z, q.w});
     }
@@ -522,18 +503,17 @@ struct Fp8DynParams {
   uint8_t* v_scales;
   int64_t ks_stride_page, ks_stride_offset, ks_stride_head;
   int64_t vs_stride_page, vs_stride_offset, vs_stride_head;
-  uint32_t group_lanes;            // lanes per scale group: 64 (per token) or head_dim / 16
   int32_t per_head;
 };
 
-// max |x| over 16 source elements; NaN elements are ignored (fmaxf), so the
-// result is a non-negative float that is never NaN.
+// max |x| over the 8 source elements of one 16-byte vector; NaN elements are
+// ignored (fmaxf), so the result is a non-negative float that is never NaN.
 template <bool kFp16>
-__device__ __forceinline__ float amax16(u32x4 a, u32x4 b) {
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+__device__ __forceinline__ float amax8(u32x4 a) {
+  const uint32_t w[4] = {a.x, a.y, a.z, a.w};
   float m = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 4; ++i) {
     float lo, hi;
     if constexpr (kFp16) {
       lo = f16_lo(w[i]); hi = f16_hi(w[i]);
@@ -582,8 +562,12 @@ __device__ __forceinline__ float dyn_scale(float amax) {
 }
 
 // Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = 2: K (0) or
-// V (1).  The wave holds the tensor's whole row: kPasses units of 16 elements
-// per lane.
+// V (1).  The wave holds the tensor's whole row: kPasses passes of 1024
+// elements, as in the static store (lane l takes 8-element groups l and
+// l + 64 of each pass).  Per token, one scale covers the row.  Per head, with
+// gph = head_dim / 8 groups per head: for gph <= 64 each head lies wholly in
+// the first or the second group of its lanes, on gph aligned lanes; for
+// gph = 128 (head_dim 1024) a head is one whole pass.
 template <int kPasses, bool kFlat, bool kFp16, typename IdxT>
 __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(const Fp8DynParams d) {
   const Fp8Params& p = d.base;
@@ -595,37 +579,50 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
   const TensorView t = tensor_view(p, is_v, token);
+  const uint32_t groups = 2u * p.units;
+  const uint32_t gph = 2u * p.units_per_head;
 
   u32x4 a[kPasses], b[kPasses];
-  uint32_t dof[kPasses];
-  float m[kPasses];
+  uint32_t da[kPasses], db[kPasses];
 #pragma unroll
-  for (int i = 0; i < kPasses; ++i) {
-    const uint32_t u = i * kWave + lane;
-    m[i] = 0.0f;
-    if (u < p.units) {
-      uint32_t sof;
-      unit_offsets<kFlat>(u, p.units_per_head, t.src_head, t.c_head, &sof, &dof[i]);
-      a[i] = load16(t.src, sof);
-      b[i] = load16(t.src, sof + 16u);
+  for (int j = 0; j < kPasses; ++j) {
+    const uint32_t g = j * (2u * kWave) + lane;
+    a[j] = u32x4{0u, 0u, 0u, 0u};
+    b[j] = u32x4{0u, 0u, 0u, 0u};
+    uint32_t so;
+    if (g < groups) {
+      group_offsets<kFlat>(g, gph, t.src_head, t.c_head, &so, &da[j]);
+      a[j] = load16(t.src, so);
+    }
+    if (g + kWave < groups) {
+      group_offsets<kFlat>(g + kWave, gph, t.src_head, t.c_head, &so, &db[j]);
+      b[j] = load16(t.src, so);
     }
   }
-  // Every lane takes part in the lane reduction below, so the bounds check comes after.
+  // Every lane takes part in the lane reductions below (groups past the row
+  // hold zeros), so the bounds check comes after them.
+  float ma[kPasses], mb[kPasses];
 #pragma unroll
-  for (int i = 0; i < kPasses; ++i) {
-    if (i * kWave + lane < p.units) m[i] = amax16<kFp16>(a[i], b[i]);
+  for (int j = 0; j < kPasses; ++j) {
+    ma[j] = amax8<kFp16>(a[j]);
+    mb[j] = amax8<kFp16>(b[j]);
   }
   if (!d.per_head) {
-    // one group: the whole row
-    float mx = m[0];
+    float mx = 0.0f;
 #pragma unroll
-    for (int i = 1; i < kPasses; ++i) mx = __builtin_fmaxf(mx, m[i]);
+    for (int j = 0; j < kPasses; ++j) mx = __builtin_fmaxf(mx, __builtin_fmaxf(ma[j], mb[j]));
     mx = group_max(mx, kWave);
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) m[i] = mx;
+    for (int j = 0; j < kPasses; ++j) ma[j] = mb[j] = mx;
+  } else if (gph > kWave) {
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) ma[j] = mb[j] = group_max(__builtin_fmaxf(ma[j], mb[j]), kWave);
   } else {
 #pragma unroll
-    for (int i = 0; i < kPasses; ++i) m[i] = group_max(m[i], d.group_lanes);
+    for (int j = 0; j < kPasses; ++j) {
+      ma[j] = group_max(ma[j], gph);
+      mb[j] = group_max(mb[j], gph);
+    }
   }
 
   if (loc < 0 || loc >= p.size_limit) {
@@ -645,19 +642,26 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
                          : d.k_scales + page * d.ks_stride_page + off * d.ks_stride_offset;
   const int64_t s_head = is_v ? d.vs_stride_head : d.ks_stride_head;
 #pragma unroll
-  for (int i = 0; i < kPasses; ++i) {
-    const uint32_t u = i * kWave + lane;
-    if (u < p.units) {
-      const float sc = dyn_scale(m[i]);
-      const float inv = 1.0f / sc;
-      // inv is finite and non-zero unless the group holds an infinity
-      store16_sc1(dst, dof[i], quantize16<kFp16, false>(a[i], b[i], inv, inv != 0.0f));
-      // One lane per group writes its scale: the first lane of each head
-      // (per head, g < num_heads), or unit 0 alone (per token, g = 0).
-      if (d.per_head ? (u & (d.group_lanes - 1)) == 0 : u == 0) {
-        const uint32_t g = d.per_head ? u / d.group_lanes : 0u;
-        *reinterpret_cast<float*>(scales + g * s_head) = sc;
-      }
+  for (int j = 0; j < kPasses; ++j) {
+    const uint32_t g = j * (2u * kWave) + lane;
+    if (g >= groups) continue;
+    const bool has_b = g + kWave < groups;
+    const float sa = dyn_scale(ma[j]), sb = dyn_scale(mb[j]);
+    const float ia = 1.0f / sa, ib = 1.0f / sb;
+    // the inverses are finite and non-zero unless a group holds an infinity
+    const u32x4 q = quantize16<kFp16, false>(a[j], b[j], ia, ib, ia != 0.0f && ib != 0.0f);
+    store8_sc1(dst, da[j], u32x2{q.x, q.y});
+    if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
+    // One lane per group writes its scale: lane 0 of the wave per token; per
+    // head, the first of each head's gph lanes (for gph = 128, lane 0 of the
+    // pass), for the head of each of its two groups.
+    if (!d.per_head) {
+      if (g == 0) *reinterpret_cast<float*>(scales) = sa;
+    } else if (gph > kWave) {
+      if (lane == 0) *reinterpret_cast<float*>(scales + (g / gph) * s_head) = sa;
+    } else if ((lane & (gph - 1)) == 0) {
+      *reinterpret_cast<float*>(scales + (g / gph) * s_head) = sa;
+      if (has_b) *reinterpret_cast<float*>(scales + ((g + kWave) / gph) * s_head) = sb;
     }
   }
 }
@@ -1104,7 +1108,6 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
   d.vs_stride_page = vs_stride_page_bytes;
   d.vs_stride_offset = vs_stride_offset_bytes;
   d.vs_stride_head = vs_stride_head_bytes;
-  d.group_lanes = per_head ? uph : (uint32_t)kWave;
   d.per_head = per_head ? 1 : 0;
   const bool flat = fp8_flat(d.base, head_dim);
   const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
