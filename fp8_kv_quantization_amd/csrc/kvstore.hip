@@ -829,6 +829,19 @@ bool fits(int64_t n, int64_t stride) {
   return stride == 0 || n <= INT64_MAX / stride;
 }
 
+// a + b + c <= INT64_MAX for non-negative a, b and c, without overflowing.
+bool sum_fits(int64_t a, int64_t b, int64_t c) {
+  return a <= INT64_MAX - b && a + b <= INT64_MAX - c;
+}
+
+// (n - 1) * stride + tail <= INT32_MAX, for n >= 1, stride >= 0 and
+// 0 <= tail <= INT32_MAX, without overflowing: the last of n items at the
+// given stride ends within 31 bits.
+bool span_fits_int32(int64_t n, int64_t stride, int64_t tail) {
+  if (tail > INT32_MAX) return false;
+  return stride == 0 || n - 1 <= (INT32_MAX - tail) / stride;
+}
+
 // Index type, stride (>= 1, and batch * stride * 8 bytes addressable), alignment.
 int check_index_args(const void* indices, int idx_dtype, int64_t idx_stride, uint32_t batch) {
   if (idx_dtype != KVSTORE_IDX_I32 && idx_dtype != KVSTORE_IDX_I64) return KVSTORE_ERR_DTYPE;
@@ -862,18 +875,22 @@ int fill_fp8_params(Fp8Params& p, const void* k, const void* v, void* k_cache, v
   }
   // Per-lane offsets inside one token row / one slot are 32-bit.
   const int64_t heads = num_heads;
-  if ((heads - 1) * k_stride_head_bytes + 2 * (int64_t)head_dim > INT32_MAX ||
-      (heads - 1) * v_stride_head_bytes + 2 * (int64_t)head_dim > INT32_MAX ||
-      (heads - 1) * kc_stride_head_bytes + head_dim > INT32_MAX ||
-      (heads - 1) * vc_stride_head_bytes + head_dim > INT32_MAX)
+  if (!span_fits_int32(heads, k_stride_head_bytes, 2 * (int64_t)head_dim) ||
+      !span_fits_int32(heads, v_stride_head_bytes, 2 * (int64_t)head_dim) ||
+      !span_fits_int32(heads, kc_stride_head_bytes, head_dim) ||
+      !span_fits_int32(heads, vc_stride_head_bytes, head_dim))
     return KVSTORE_ERR_SHAPE;
-  // Largest slot byte offset must fit in int64.
+  // Largest byte offset within a cache (last page, last slot of a page, plus
+  // the in-slot span of at most INT32_MAX checked above) must fit in int64,
+  // whether the slot is addressed as page/offset or linearly.
   const int64_t max_page = (size_limit - 1) / page_size;
   if (!fits(max_page + 1, kc_stride_page_bytes) || !fits(max_page + 1, vc_stride_page_bytes) ||
       !fits(page_size, kc_stride_offset_bytes) || !fits(page_size, vc_stride_offset_bytes) ||
       !fits(size_limit, kc_stride_offset_bytes) || !fits(size_limit, vc_stride_offset_bytes) ||
-      max_page * kc_stride_page_bytes > INT64_MAX - page_size * kc_stride_offset_bytes ||
-      max_page * vc_stride_page_bytes > INT64_MAX - page_size * vc_stride_offset_bytes)
+      !sum_fits(max_page * kc_stride_page_bytes, page_size * kc_stride_offset_bytes, INT32_MAX) ||
+      !sum_fits(max_page * vc_stride_page_bytes, page_size * vc_stride_offset_bytes, INT32_MAX) ||
+      !sum_fits(size_limit * kc_stride_offset_bytes, INT32_MAX, 0) ||
+      !sum_fits(size_limit * vc_stride_offset_bytes, INT32_MAX, 0))
     return KVSTORE_ERR_SHAPE;
   if (!fits(batch, k_stride_token_bytes) || !fits(batch, v_stride_token_bytes))
     return KVSTORE_ERR_SHAPE;
@@ -955,8 +972,8 @@ int fp8_paged_store(bool e5m2, const void* k, const void* v, void* k_cache, void
   const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
   const bool i64 = idx_dtype == KVSTORE_IDX_I64;
 
-  // Units of 16 elements per lane: up to 2 per lane per tensor in one wave
-  // (32 B of K + 32 B of V loaded per unit), wider rows split over blockIdx.y.
+  // Passes of 1024 elements (128 groups of 8, two per lane): up to 2 per wave,
+  // wider rows split over blockIdx.y.
   const int64_t waves_units = ceil_div(p.units, kWave);
   const int passes = waves_units >= 2 ? 2 : 1;
   const int64_t slices = ceil_div(waves_units, passes);
@@ -1094,10 +1111,10 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
   if (!fits(max_page + 1, ks_stride_page_bytes) || !fits(max_page + 1, vs_stride_page_bytes) ||
       !fits(page_size, ks_stride_offset_bytes) || !fits(page_size, vs_stride_offset_bytes) ||
       !fits(groups, ks_stride_head_bytes) || !fits(groups, vs_stride_head_bytes) ||
-      max_page * ks_stride_page_bytes > INT64_MAX / 2 - page_size * ks_stride_offset_bytes -
-                                            groups * ks_stride_head_bytes ||
-      max_page * vs_stride_page_bytes > INT64_MAX / 2 - page_size * vs_stride_offset_bytes -
-                                            groups * vs_stride_head_bytes)
+      !sum_fits(max_page * ks_stride_page_bytes, page_size * ks_stride_offset_bytes,
+                groups * ks_stride_head_bytes) ||
+      !sum_fits(max_page * vs_stride_page_bytes, page_size * vs_stride_offset_bytes,
+                groups * vs_stride_head_bytes))
     return KVSTORE_ERR_SHAPE;
 
   d.k_scales = reinterpret_cast<uint8_t*>(k_scale_cache);

@@ -139,6 +139,15 @@ FP8_BAD = [
     ("stride_misaligned", dict(v_stride_head_bytes=264), -3),
     ("cache_stride_misaligned", dict(vc_stride_offset_bytes=1032), -3),
     ("head_offsets_over_32bit", dict(kc_stride_head_bytes=1 << 30), -2),
+    # (heads - 1) * head stride beyond int64: must not wrap into a passing value
+    ("head_stride_product_overflow", dict(num_heads=1 << 20, head_dim=16,
+                                          k_stride_head_bytes=1 << 50), -2),
+    ("cache_head_stride_product_overflow", dict(num_heads=1 << 20, head_dim=16,
+                                                vc_stride_head_bytes=(1 << 62) + 16), -2),
+    # slot offset plus the in-slot head span beyond int64
+    ("slot_plus_head_span_overflow", dict(size_limit=64, kc_stride_page_bytes=64 * ((1 << 57) - 16),
+                                          kc_stride_offset_bytes=(1 << 57) - 16,
+                                          kc_stride_head_bytes=1 << 27), -2),
     ("slot_offset_overflow", dict(kc_stride_page_bytes=1 << 60, size_limit=1 << 20), -2),
     ("scale_misaligned", dict(inv_k_scale_ptr=A + 2), -3),
     ("cache_misaligned", dict(v_cache=A + 8), -3),
@@ -229,6 +238,9 @@ DYN_BAD = [
     ("scale_stride_misaligned", dict(vs_stride_offset_bytes=34), -3),
     ("scale_stride_negative", dict(ks_stride_head_bytes=-4), -2),
     ("scale_offset_overflow", dict(ks_stride_page_bytes=1 << 61, size_limit=1 << 20), -2),
+    # offset + head terms each within int64, their sum not (must not wrap)
+    ("scale_offset_sum_overflow", dict(size_limit=64, ks_stride_offset_bytes=(1 << 57) - 4,
+                                       ks_stride_head_bytes=(1 << 60) - 4), -2),
     ("inherits_fp8_checks", dict(head_dim=120), -2),
 ]
 
