@@ -11,8 +11,9 @@ cache), so the figure is an HBM figure, not a cache figure.  The metric is
 effective bandwidth: algorithmic bytes (K/V rows read + indices read + cache
 rows written, + the two fp32 scales) per second.
 
-Prints one JSON line.  ``--gpus N`` with N > 1 exits: this build measures one
-GPU only.
+Prints one JSON line.  ``--gpus N`` with N > 1 exits with a message: the
+benchmark measures one GPU (the store needs no exchange between GPUs, so each
+GPU of a larger job runs this same step on its own share).
 """
 from __future__ import annotations
 
@@ -78,8 +79,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
-              "supported by this build", file=sys.stderr)
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported; the store shards with no exchange, so each GPU would run this "
+              "same one-GPU step on its own share", file=sys.stderr)
         sys.exit(2)
 
     import torch
