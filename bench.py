@@ -205,14 +205,19 @@ def main():
     fp8_us = fp8_ms_total * 1e3 / K
     value = (b3 + b4) / (ms_per_step * 1e-3) / 1e9
 
-    decode = None
+    decode = tiny = None
     if not args.no_decode:
-        decode = bench_decode(kv, torch, dev, kvgen, to_dev)
+        decode = bench_decode(kv, torch, dev, kvgen, to_dev, 2,
+                              "decode copy (256 tok, 8x128 bf16, int64, 2^20 slots)")
+        tiny = bench_decode(kv, torch, dev, kvgen, to_dev, 1,
+                            "tiny copy (16 tok, 2x64 bf16, int32, 256 slots)")
 
     next_rows = None
     if not args.no_next:
         next_rows = bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh)
         next_rows.update(bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh))
+
+    wide = bench_wide_strided(kv, torch, dev, kvgen, to_dev)
 
     traffic = stored_traffic()
     roofline = {
@@ -268,6 +273,8 @@ def main():
         "roofline": roofline,
         "breakdown": breakdown,
         "decode_copy": decode,
+        "tiny_copy": tiny,
+        "wide_strided_copy": wide,
         "next_rows": next_rows,
         "cpu_baseline": cpu,
     }
@@ -392,18 +399,19 @@ def bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh, n=100):
         "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
 
 
-def bench_decode(kv, torch, dev, kvgen, to_dev):
-    """Decode copy (256 tokens, 2 KiB rows, int64, 2^20 slots): per-call time
-    back to back, single-call latency, and per-call time when the calls are
-    replayed from a captured HIP graph (how a serving loop issues them), all
-    from HIP events."""
-    c2 = kvgen.workload(2)
+def bench_decode(kv, torch, dev, kvgen, to_dev, n_workload, label):
+    """A launch-bound copy (workload 1: tiny copy, 2: decode copy): per-call
+    time back to back, single-call latency, and per-call time when the calls
+    are replayed from a captured HIP graph (how a serving loop issues them),
+    all from HIP events, over 16 disjoint index sets."""
+    c2 = kvgen.workload(n_workload)
     S = 16
     sets = kvgen.disjoint_index_sets(c2, S)
     k = to_dev(c2.k)
     v = to_dev(c2.v)
     idx = [to_dev(a) for a in sets]
     R = c2.row_bytes
+    code = kv.IDX_I64 if c2.indices.dtype == np.int64 else kv.IDX_I32
     kc = torch.full((c2.slots, R), 0xFF, dtype=torch.uint8, device=dev)
     vc = torch.full_like(kc, 0xFF)
     stream = torch.cuda.current_stream()
@@ -411,8 +419,9 @@ def bench_decode(kv, torch, dev, kvgen, to_dev):
 
     def call(s, on=None):
         st = kv.kvstore_copy(k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
-                             idx[s].data_ptr(), kv.IDX_I64, 1, R, R, R, R, c2.num_tokens,
-                             c2.slots, sh if on is None else on)
+                             idx[s].data_ptr(), code, 1, R, c2.in_stride_bytes,
+                             c2.in_stride_bytes, R, c2.num_tokens, c2.slots,
+                             sh if on is None else on)
         if st:
             raise kv.KVStoreError(st, "kvstore_copy")
 
@@ -455,11 +464,58 @@ def bench_decode(kv, torch, dev, kvgen, to_dev):
     st, _, _ = kv.kvstore_check_error(sh)
     assert st == kv.OK
     del kc, vc
-    return {"workload": "decode copy (256 tok, 8x128 bf16, int64, 2^20 slots)",
+    return {"workload": label,
             "us_per_call_back_to_back": round(b2b_us, 3),
             "us_single_call_median": round(statistics.median(lat), 3),
             "us_per_call_graph_replay": round(graph_us, 3),
             "bytes": c2.algorithmic_bytes()}
+
+
+def bench_wide_strided(kv, torch, dev, kvgen, to_dev, S=16, n=50):
+    """Wide strided copy (8192 tokens, 1x576 fp16 = 1152 B rows read at a
+    1280 B row stride, int64, 2^19 slots): average launch time over S
+    disjoint input/index sets (about 600 MB per cycle, above the last-level
+    cache)."""
+    c5 = kvgen.workload(5)
+    sets = kvgen.disjoint_index_sets(c5, S)
+    k = [to_dev(c5.k)]
+    v = [to_dev(c5.v)]
+    for s in range(1, S):
+        k.append(torch.roll(k[0], s * 997, 0).contiguous())
+        v.append(torch.roll(v[0], s * 997, 0).contiguous())
+    idx = [to_dev(a) for a in sets]
+    R = c5.row_bytes
+    kc = torch.full((c5.slots, R), 0xFF, dtype=torch.uint8, device=dev)
+    vc = torch.full_like(kc, 0xFF)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def call(s):
+        st = kv.kvstore_copy(k[s].data_ptr(), v[s].data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                             idx[s].data_ptr(), kv.IDX_I64, 1, R, c5.in_stride_bytes,
+                             c5.in_stride_bytes, R, c5.num_tokens, c5.slots, sh)
+        if st:
+            raise kv.KVStoreError(st, "kvstore_copy")
+
+    for i in range(S):
+        call(i % S)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        call(i % S)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    st, _, _ = kv.kvstore_check_error(sh)
+    assert st == kv.OK
+    b = c5.algorithmic_bytes()
+    del kc, vc, k, v
+    return {"workload": "wide strided copy (8192 tok, 1x576 fp16, input row stride 640 elements, "
+                        "int64, 2^19 slots)",
+            "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+            "rotation_sets": S}
 
 
 def cpu_baseline(c3, c4, reps):

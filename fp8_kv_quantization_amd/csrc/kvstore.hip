@@ -23,8 +23,9 @@
 //   * the row base addresses are wave-uniform 64-bit values (scalar registers)
 //     and the per-lane offset is a 32-bit vector register;
 //   * copy: cache rows are written with non-temporal stores, and residency is
-//     capped near 8 waves per CU (see copy_blocks_per_cu): the rows land at
-//     scattered slots, and fewer concurrent write streams measured faster;
+//     capped to about 32 KiB of loads in flight per CU (8 waves of 2 KiB rows;
+//     see copy_waves_per_cu): the rows land at scattered slots, and fewer
+//     concurrent write streams measured faster;
 //   * fp8: the quantised rows are written with the sc1 cache policy through a
 //     per-row buffer descriptor, at full occupancy (the conversion needs the
 //     latency hiding);
@@ -690,13 +691,16 @@ int launch(void (*kernel)(Args...), dim3 grid, dim3 block, uint32_t lds_bytes,
              : KVSTORE_ERR_HIP;
 }
 
-// Resident copy blocks per CU: about 8 waves per CU.  The copy writes rows
-// at scattered slots; with every wave slot filled (32 per CU) the scattered
-// write streams measured ~5% slower than with 6-10 waves per CU, which still
-// keep 24-40 KiB of loads in flight per CU.  Rows of one chunk move half the
-// bytes per wave, so they get twice the waves.
-constexpr int copy_blocks_per_cu(int chunks_per_wave) {
-  return (chunks_per_wave == 1 ? 16 : 8) / kCopyWavesPerBlock;
+// Resident copy waves per CU: enough for about 32 KiB of loads in flight per
+// CU, at least 8 and at most 32 (every wave slot).  The copy writes rows at
+// scattered slots; with every wave slot filled the scattered write streams of
+// the 2 KiB-row prefill copy measured ~5% slower than with 6-10 waves per CU
+// (8 waves x 4 KiB), while rows that move fewer bytes per wave need more waves
+// to keep the loads in flight (1152-byte rows: 14 waves, 4.6% faster than 8).
+constexpr int64_t kCopyLoadBytesPerCU = 32768;
+inline int64_t copy_waves_per_cu(int64_t load_bytes_per_wave) {
+  const int64_t w = (kCopyLoadBytesPerCU + load_bytes_per_wave / 2) / load_bytes_per_wave;
+  return w < 8 ? 8 : w > 32 ? 32 : w;
 }
 
 // Tokens of one launch.  A grid with one wave per token then stays at 2^30
@@ -759,9 +763,13 @@ int launch_copy_vw(const CopyParams& p, hipStream_t stream) {
   if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
   const dim3 grid((uint32_t)ceil_div(p.batch, kCopyWavesPerBlock), (uint32_t)slices);
   // The kernel uses no LDS; the dynamic allocation only caps residency (tuned
-  // for 16-byte lanes, where a wave has the most bytes in flight).
+  // for 16-byte lanes, where a wave has the most bytes in flight).  A wave
+  // loads the K and V bytes of its row slice.
   const int64_t lds = VW == 16 ? lds_per_cu() : 0;
-  const uint32_t lds_bytes = lds > 0 ? (uint32_t)(lds / copy_blocks_per_cu(per_wave)) : 0;
+  const int64_t slice_bytes = (int64_t)per_wave * kChunk;
+  const int64_t wave_bytes = 2 * (p.row_bytes < slice_bytes ? (int64_t)p.row_bytes : slice_bytes);
+  const int64_t blocks_per_cu = copy_waves_per_cu(wave_bytes) / kCopyWavesPerBlock;
+  const uint32_t lds_bytes = lds > 0 ? (uint32_t)(lds / blocks_per_cu) : 0;
   switch (per_wave) {
     case 1: return launch(kvstore_copy_kernel<VW, 1, IdxT>, grid, block, lds_bytes, stream, p);
     case 2: return launch(kvstore_copy_kernel<VW, 2, IdxT>, grid, block, lds_bytes, stream, p);
