@@ -46,10 +46,12 @@ def _copy(lib):
     kc = np.full((128, R), 0xFF, dtype=np.uint8)
     vc = np.full_like(kc, 0xFF)
     kb = np.ascontiguousarray(c.k).view(np.uint8)
-    vb = np.ascontiguousarray(c.v).view(np.uint8)
+    # V rows at their own stride (64 bytes wider than K's), padding poisoned
+    vb = np.full((40, c.in_stride_bytes + 64), 0xAB, dtype=np.uint8)
+    vb[:, :c.in_stride_bytes] = np.ascontiguousarray(c.v).view(np.uint8)
     st = oracle.copy(kb, vb, kc, vc, strided, row_bytes=R, k_stride=c.in_stride_bytes,
-                     v_stride=c.in_stride_bytes, cache_stride=R, size_limit=limit, idx_stride=2,
-                     batch=40, lib=lib)
+                     v_stride=c.in_stride_bytes + 64, cache_stride=R, size_limit=limit,
+                     idx_stride=2, batch=40, lib=lib)
     good = [t for t in range(40) if t not in (7, 30)]
     return (st == (38, 7, 2) and np.all(kc[limit:] == 0xFF)
             and np.array_equal(kc[idx[good]], kb[good, :R])
@@ -64,26 +66,29 @@ def _fp8(lib):
     keep = c.indices < slots
     idx = c.indices[keep].copy()
     T = idx.size
-    sh_in = D + 8
+    # K and V each with their own input head padding and cache layout
+    sh_in, sh_in_v = D + 8, D + 24
     bk = np.full((T, H, sh_in), kvgen.PAD_POISON, dtype=np.uint16)
-    bv = np.full_like(bk, kvgen.PAD_POISON)
+    bv = np.full((T, H, sh_in_v), kvgen.PAD_POISON, dtype=np.uint16)
     bk[:, :, :D] = c.k[keep].reshape(T, H, D)
     bv[:, :, :D] = c.v[keep].reshape(T, H, D)
-    sh = D + 16
-    so = H * sh + 32
-    sp = P * so + 512
+    sh, sh_v = D + 16, D + 48
+    so, so_v = H * sh + 32, H * sh_v + 16
+    sp, sp_v = P * so + 512, P * so_v + 256
     pages = slots // P
     kc = np.full(pages * sp, 0xFF, dtype=np.uint8)
-    vc = np.full_like(kc, 0xFF)
+    vc = np.full(pages * sp_v, 0xFF, dtype=np.uint8)
     st = oracle.fp8_paged(bk, bv, kc, vc, idx, src_dtype="bf16", num_heads=H, head_dim=D,
-                          k_strides=(H * sh_in * 2, sh_in * 2), v_strides=(H * sh_in * 2, sh_in * 2),
-                          kc_strides=(sp, so, sh), vc_strides=(sp, so, sh), size_limit=slots,
+                          k_strides=(H * sh_in * 2, sh_in * 2),
+                          v_strides=(H * sh_in_v * 2, sh_in_v * 2),
+                          kc_strides=(sp, so, sh), vc_strides=(sp_v, so_v, sh_v), size_limit=slots,
                           page_size=P, inv_k_bits=c.inv_k_bits, inv_v_bits=c.inv_v_bits, lib=lib)
     if st != (T, -1, 0):
         return False
     ok = True
-    for cache, src, inv in ((kc, c.k[keep], c.inv_k_bits), (vc, c.v[keep], c.inv_v_bits)):
-        view = np.lib.stride_tricks.as_strided(cache, shape=(pages, P, H, D), strides=(sp, so, sh, 1))
+    for cache, src, inv, (cp, co, ch) in ((kc, c.k[keep], c.inv_k_bits, (sp, so, sh)),
+                                          (vc, c.v[keep], c.inv_v_bits, (sp_v, so_v, sh_v))):
+        view = np.lib.stride_tricks.as_strided(cache, shape=(pages, P, H, D), strides=(cp, co, ch, 1))
         loc = idx.astype(np.int64)
         got = view[loc // P, loc % P].reshape(T, H * D)
         ok &= np.array_equal(got, _ref.expected_codes(src, "bf16", inv))
@@ -102,6 +107,37 @@ def _dynamic(lib):
             ok &= st == (60, -1, 0) and np.array_equal(cache[idx], codes) \
                 and np.array_equal(scales[idx], sc.view(np.uint32))
     return bool(ok)
+
+
+def _dynamic_layouts(lib):
+    """Per-head dynamic scales with K and V in different layouts: V input heads
+    padded, V cache slots and heads padded, V scales at their own strides."""
+    c = kvgen.workload(4, tokens=60, slots=2 * 64)
+    H, D, P, T = 8, 128, 64, 60
+    slots = c.slots
+    idx = c.indices.astype(np.int64)
+    shv = D + 16
+    bv = np.full((T, H, shv), kvgen.PAD_POISON, dtype=np.uint16)
+    bv[:, :, :D] = c.v.reshape(T, H, D)
+    kc = np.full((slots, H * D), 0xFF, dtype=np.uint8)
+    vsh, vso = D + 32, H * (D + 32) + 64
+    vc = np.full(slots * vso, 0xFF, dtype=np.uint8)
+    ks = np.full((slots, H), 0xFFFFFFFF, dtype=np.uint32)
+    vs = np.full((slots, 2 * H), 0xFFFFFFFF, dtype=np.uint32)   # V: head stride 8 bytes
+    st = oracle.fp8_paged_dynamic(
+        c.k, bv, kc, vc, c.indices, ks, vs, src_dtype="bf16", num_heads=H, head_dim=D,
+        k_strides=(H * D * 2, D * 2), v_strides=(H * shv * 2, shv * 2),
+        kc_strides=(P * H * D, H * D, D), vc_strides=(P * vso, vso, vsh),
+        ks_strides=(P * H * 4, H * 4, 4), vs_strides=(P * 2 * H * 4, 2 * H * 4, 8),
+        per_head=True, size_limit=slots, page_size=P, lib=lib)
+    codes_k, sc_k = _ref.dynamic_expected(c.k, "bf16", H, D, True)
+    codes_v, sc_v = _ref.dynamic_expected(c.v, "bf16", H, D, True)
+    vview = np.lib.stride_tricks.as_strided(vc, shape=(slots, H, D), strides=(vso, vsh, 1))
+    return bool(st == (T, -1, 0) and np.array_equal(kc[idx], codes_k)
+                and np.array_equal(vview[idx].reshape(T, H * D), codes_v)
+                and np.array_equal(ks[idx], sc_k.view(np.uint32))
+                and np.array_equal(vs[idx][:, ::2], sc_v.view(np.uint32))
+                and np.all(vs[:, 1::2] == 0xFFFFFFFF))
 
 
 def _decode(lib, src):
@@ -136,6 +172,7 @@ CHECKS = {
     "copy_store": _copy,
     "fp8_store": _fp8,
     "fp8_dynamic": _dynamic,
+    "fp8_dynamic_layouts": _dynamic_layouts,
     "e5m2": _e5m2,
 }
 

@@ -50,35 +50,35 @@ def trial_copy(rng):
     row = int(rng.integers(1, 700)) * 4
     row -= row % vw
     row = max(row, vw)
-    pad = int(rng.integers(0, 4)) * vw
-    stride = row + pad
+    k_stride = row + int(rng.integers(0, 4)) * vw        # K and V rows at their own strides
+    v_stride = row + int(rng.integers(0, 4)) * vw
     T = int(rng.integers(1, 1500))
     slots = T + int(rng.integers(2, 400))
     limit = slots - int(rng.integers(0, 3))          # >= T: every token has an index
     dtype = np.int64 if rng.integers(0, 2) else np.int32
     istride = int(rng.integers(1, 4))
     idx = _indices(rng, T, limit, float(rng.choice([0.0, 0.0, 0.02])), dtype)
-    kb = rng.integers(0, 256, (T, stride), dtype=np.uint8)
-    vb = rng.integers(0, 256, (T, stride), dtype=np.uint8)
+    kb = rng.integers(0, 256, (T, k_stride), dtype=np.uint8)
+    vb = rng.integers(0, 256, (T, v_stride), dtype=np.uint8)
     off = int(rng.choice([0, vw]))
-    _say(f"copy row={row} stride={stride} T={T} slots={slots} limit={limit} vw={vw} "
-         f"{dtype.__name__} istride={istride} off={off}")
-    kd = torch.zeros(T * stride + 64, dtype=torch.uint8, device=DEV)
-    vd = torch.zeros_like(kd)
-    kd[off:off + T * stride] = _dev(kb.reshape(-1))
-    vd[off:off + T * stride] = _dev(vb.reshape(-1))
+    _say(f"copy row={row} strides={k_stride},{v_stride} T={T} slots={slots} limit={limit} "
+         f"vw={vw} {dtype.__name__} istride={istride} off={off}")
+    kd = torch.zeros(T * k_stride + 64, dtype=torch.uint8, device=DEV)
+    vd = torch.zeros(T * v_stride + 64, dtype=torch.uint8, device=DEV)
+    kd[off:off + T * k_stride] = _dev(kb.reshape(-1))
+    vd[off:off + T * v_stride] = _dev(vb.reshape(-1))
     kc = torch.full((slots * row + 64,), 0xFF, dtype=torch.uint8, device=DEV)
     vc = torch.full_like(kc, 0xFF)
     di = _dev(_strided_indices(rng, idx, istride))
     st = kv.kvstore_copy(kd.data_ptr() + off, vd.data_ptr() + off, kc.data_ptr() + off,
                          vc.data_ptr() + off, di.data_ptr(),
-                         kv.IDX_I64 if dtype == np.int64 else kv.IDX_I32, istride, row, stride,
-                         stride, row, T, limit, stream())
+                         kv.IDX_I64 if dtype == np.int64 else kv.IDX_I32, istride, row, k_stride,
+                         v_stride, row, T, limit, stream())
     assert st == kv.OK
     okc = np.full(slots * row + 64, 0xFF, dtype=np.uint8)
     ovc = np.full_like(okc, 0xFF)
-    ost = oracle.copy(kb, vb, okc[off:], ovc[off:], idx, row_bytes=row, k_stride=stride,
-                      v_stride=stride, cache_stride=row, size_limit=limit)
+    ost = oracle.copy(kb, vb, okc[off:], ovc[off:], idx, row_bytes=row, k_stride=k_stride,
+                      v_stride=v_stride, cache_stride=row, size_limit=limit)
     return [(kc, okc), (vc, ovc)], ost
 
 
@@ -102,39 +102,45 @@ def trial_fp8(rng, op):
     dtype = np.int64 if rng.integers(0, 2) else np.int32
     istride = int(rng.integers(1, 3))
     idx = _indices(rng, T, limit, float(rng.choice([0.0, 0.0, 0.03])), dtype)
-    # input [T, H, D + in_pad] elements, cache [pages, P, H, D + c_pad] bytes + page padding
-    in_pad = int(rng.choice([0, 8, 16]))
-    c_pad = int(rng.choice([0, 16, 32]))
-    page_pad = int(rng.choice([0, 16, 4096]))
-    sh_in = D + in_pad
-    bits = rng.integers(0, 65536, (2, T, H, sh_in), dtype=np.uint32).astype(np.uint16)
-    # mostly ordinary magnitudes, some raw patterns (NaN / inf / subnormal)
-    ordinary = rng.standard_normal((2, T, H, sh_in)).astype(np.float32) * np.float32(
-        rng.choice([1.0, 30.0, 3000.0]))
-    if src == "bf16":
-        u = ordinary.view(np.uint32)
-        ob = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
-    else:
-        ob = ordinary.astype(np.float16).view(np.uint16)
-    raw = rng.random((2, T, H, sh_in)) < 0.01
-    bits = np.where(raw, bits, ob).astype(np.uint16)
-    kb, vb = bits[0], bits[1]
-    sh = D + c_pad
-    so = H * sh
-    sp = P * so + page_pad
+    # K and V each: input [T, H, D + in_pad] elements, cache [pages, P, H, D +
+    # c_pad] bytes + page padding, padding drawn separately for K and V
+    scale_mag = np.float32(rng.choice([1.0, 30.0, 3000.0]))
+
+    def draw_input():
+        sh_in = D + int(rng.choice([0, 8, 16]))
+        raw_bits = rng.integers(0, 65536, (T, H, sh_in), dtype=np.uint32).astype(np.uint16)
+        # mostly ordinary magnitudes, some raw patterns (NaN / inf / subnormal)
+        ordinary = rng.standard_normal((T, H, sh_in)).astype(np.float32) * scale_mag
+        if src == "bf16":
+            u = ordinary.view(np.uint32)
+            ob = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+        else:
+            ob = ordinary.astype(np.float16).view(np.uint16)
+        raw = rng.random((T, H, sh_in)) < 0.01
+        return np.where(raw, raw_bits, ob).astype(np.uint16), sh_in
+
+    def draw_cache():
+        sh = D + int(rng.choice([0, 16, 32]))
+        so = H * sh + int(rng.choice([0, 0, 16]))
+        return (P * so + int(rng.choice([0, 16, 4096])), so, sh)
+
+    kb, sh_in_k = draw_input()
+    vb, sh_in_v = draw_input()
+    kcs, vcs = draw_cache(), draw_cache()
     scales = [None, 0x3ECCCCCD, 0x3F169696, 0x41200000, 0x3A83126F]
     ik = scales[int(rng.integers(0, len(scales)))]
     iv = scales[int(rng.integers(0, len(scales)))]
     _say(f"{op} T={T} H={H} D={D} src={src} P={P} pages={pages} limit={limit} "
-         f"{dtype.__name__} istride={istride} pads={in_pad},{c_pad},{page_pad} ik={ik} iv={iv}")
+         f"{dtype.__name__} istride={istride} in={sh_in_k},{sh_in_v} kc={kcs} vc={vcs} "
+         f"ik={ik} iv={iv}")
     kd, vd = _dev(kb), _dev(vb)
-    kc = torch.full((pages * sp,), 0xFF, dtype=torch.uint8, device=DEV)
-    vc = torch.full_like(kc, 0xFF)
+    kc = torch.full((pages * kcs[0],), 0xFF, dtype=torch.uint8, device=DEV)
+    vc = torch.full((pages * vcs[0],), 0xFF, dtype=torch.uint8, device=DEV)
     di = _dev(_strided_indices(rng, idx, istride))
-    okc = np.full(pages * sp, 0xFF, dtype=np.uint8)
-    ovc = np.full_like(okc, 0xFF)
-    in_s = (H * sh_in * 2, sh_in * 2)
-    c_s = (sp, so, sh)
+    okc = np.full(pages * kcs[0], 0xFF, dtype=np.uint8)
+    ovc = np.full(pages * vcs[0], 0xFF, dtype=np.uint8)
+    k_in = (H * sh_in_k * 2, sh_in_k * 2)
+    v_in = (H * sh_in_v * 2, sh_in_v * 2)
     idt = kv.IDX_I64 if dtype == np.int64 else kv.IDX_I32
     sdt = kv.SRC_FP16 if src == "fp16" else kv.SRC_BF16
     if not dynamic:
@@ -142,35 +148,38 @@ def trial_fp8(rng, op):
         ivd = _dev(np.array([iv], dtype=np.uint32).view(np.float32)) if iv is not None else None
         entry = kv.kvstore_fp8_paged_e5m2 if op == "e5m2" else kv.kvstore_fp8_paged
         st = entry(kd.data_ptr(), vd.data_ptr(), kc.data_ptr(), vc.data_ptr(), di.data_ptr(), idt,
-                   istride, sdt, H, D, *in_s, *in_s, *c_s, *c_s, T, limit, P,
+                   istride, sdt, H, D, *k_in, *v_in, *kcs, *vcs, T, limit, P,
                    None if ikd is None else ikd.data_ptr(), None if ivd is None else ivd.data_ptr(),
                    stream())
         torch.cuda.synchronize()
         assert st == kv.OK
         ost = oracle.fp8_paged(kb, vb, okc, ovc, idx, src_dtype=src, num_heads=H, head_dim=D,
-                               k_strides=in_s, v_strides=in_s, kc_strides=c_s, vc_strides=c_s,
+                               k_strides=k_in, v_strides=v_in, kc_strides=kcs, vc_strides=vcs,
                                size_limit=limit, page_size=P, inv_k_bits=ik, inv_v_bits=iv,
                                fmt="e5m2" if op == "e5m2" else "e4m3fn")
         return [(kc, okc), (vc, ovc)], ost
     G = H if per_head else 1
-    s_head = 4 + 4 * int(rng.integers(0, 2)) if per_head else 0
-    s_off = G * max(s_head, 4) + 4 * int(rng.integers(0, 3))
-    s_page = P * s_off + 4 * int(rng.integers(0, 5))
-    ks = torch.full((pages * s_page + 16,), 0xFF, dtype=torch.uint8, device=DEV)
-    vs = torch.full_like(ks, 0xFF)
-    oks = np.full(pages * s_page + 16, 0xFF, dtype=np.uint8)
-    ovs = np.full_like(oks, 0xFF)
-    ss = (s_page, s_off, s_head)
+
+    def draw_scales():
+        s_head = 4 + 4 * int(rng.integers(0, 2)) if per_head else 0
+        s_off = G * max(s_head, 4) + 4 * int(rng.integers(0, 3))
+        return (P * s_off + 4 * int(rng.integers(0, 5)), s_off, s_head)
+
+    kss, vss = draw_scales(), draw_scales()
+    ks = torch.full((pages * kss[0] + 16,), 0xFF, dtype=torch.uint8, device=DEV)
+    vs = torch.full((pages * vss[0] + 16,), 0xFF, dtype=torch.uint8, device=DEV)
+    oks = np.full(pages * kss[0] + 16, 0xFF, dtype=np.uint8)
+    ovs = np.full(pages * vss[0] + 16, 0xFF, dtype=np.uint8)
     st = kv.kvstore_fp8_paged_dynamic(
         kd.data_ptr(), vd.data_ptr(), kc.data_ptr(), vc.data_ptr(), di.data_ptr(), idt, istride,
-        sdt, H, D, *in_s, *in_s, *c_s, *c_s, ks.data_ptr(), vs.data_ptr(),
-        kv.SCALE_PER_TOKEN_HEAD if per_head else kv.SCALE_PER_TOKEN, *ss, *ss, T, limit, P,
+        sdt, H, D, *k_in, *v_in, *kcs, *vcs, ks.data_ptr(), vs.data_ptr(),
+        kv.SCALE_PER_TOKEN_HEAD if per_head else kv.SCALE_PER_TOKEN, *kss, *vss, T, limit, P,
         stream())
     torch.cuda.synchronize()
     assert st == kv.OK
     ost = oracle.fp8_paged_dynamic(kb, vb, okc, ovc, idx, oks, ovs, src_dtype=src, num_heads=H,
-                                   head_dim=D, k_strides=in_s, v_strides=in_s, kc_strides=c_s,
-                                   vc_strides=c_s, ks_strides=ss, vs_strides=ss,
+                                   head_dim=D, k_strides=k_in, v_strides=v_in, kc_strides=kcs,
+                                   vc_strides=vcs, ks_strides=kss, vs_strides=vss,
                                    per_head=per_head, size_limit=limit, page_size=P)
     return [(kc, okc), (vc, ovc), (ks, oks), (vs, ovs)], ost
 

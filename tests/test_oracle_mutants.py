@@ -54,6 +54,18 @@ MUTANTS = {
     "dyn_wrong_fp8_max": ("float scale = amax / 448.0f;", "float scale = amax / 480.0f;"),
     "dyn_scale_page_offset_swapped": ("scales + page * sc_page + off * sc_off + g * sc_head",
                                       "scales + off * sc_page + page * sc_off + g * sc_head"),
+    # V borrowing one of K's layout parameters
+    "copy_v_uses_k_stride": ("v + t * v_stride", "v + t * k_stride"),
+    "fp8_v_uses_k_input_strides": ("store_fp8_row(v, v_stride_token, v_stride_head,",
+                                   "store_fp8_row(v, k_stride_token, k_stride_head,"),
+    "fp8_vcache_uses_k_layout": ("vc_stride_offset, vc_stride_head, page, off",
+                                 "kc_stride_offset, kc_stride_head, page, off"),
+    "dyn_v_uses_k_input_stride": ("int64_t s_tok = x ? v_stride_token : k_stride_token;",
+                                  "int64_t s_tok = k_stride_token;"),
+    "dyn_v_uses_k_cache_layout": ("int64_t c_off = x ? vc_stride_offset : kc_stride_offset;",
+                                  "int64_t c_off = kc_stride_offset;"),
+    "dyn_v_uses_k_scale_layout": ("int64_t sc_head = x ? vs_stride_head : ks_stride_head;",
+                                  "int64_t sc_head = ks_stride_head;"),
 }
 
 

@@ -296,3 +296,14 @@ def test_fp8_out_of_bounds_rows_are_skipped_and_counted():
                           inv_v_bits=c.inv_v_bits)
     assert st == (126, 0, 2)
     assert np.all(kc[limit:] == 0xFF) and np.all(vc[limit:] == 0xFF)
+
+
+def test_k_and_v_layouts_are_independent():
+    """K and V inputs, caches and scale caches each at their own strides: a V
+    that borrowed one of K's strides would read or write the wrong bytes
+    (copy, fused FP8 and per-head dynamic-scale stores)."""
+    from tests import _battery
+    lib = oracle.load()
+    assert _battery._copy(lib)
+    assert _battery._fp8(lib)
+    assert _battery._dynamic_layouts(lib)
