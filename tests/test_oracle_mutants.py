@@ -66,6 +66,7 @@ MUTANTS = {
                                   "int64_t c_off = kc_stride_offset;"),
     "dyn_v_uses_k_scale_layout": ("int64_t sc_head = x ? vs_stride_head : ks_stride_head;",
                                   "int64_t sc_head = ks_stride_head;"),
+    "fp8_v_uses_k_inverse_scale": ("src_is_fp16, iv, fmt);", "src_is_fp16, ik, fmt);"),
 }
 
 
