@@ -90,9 +90,9 @@ def trial_fp8(rng, op):
         H = int(rng.integers(1, max(2, 4096 // D // 2) + 1))
     else:
         D = int(rng.integers(1, 17)) * 16
-        H = int(rng.integers(1, 9))
-        if dynamic:
-            H = min(H, 4096 // D)
+        # static stores up to 24 heads (up to 6144 elements: rows split over
+        # grid slices); dynamic scales keep the whole row in one wave
+        H = int(rng.integers(1, 25)) if not dynamic else min(int(rng.integers(1, 9)), 4096 // D)
     src = "fp16" if rng.integers(0, 2) else "bf16"
     T = int(rng.integers(1, 800))
     P = int(rng.choice([1, 3, 16, 48, 64, 100]))
