@@ -281,6 +281,28 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def time_calls(torch, call, S, n=50, reps=3, warm=500):
+    """Median over `reps` windows of the average time of `n` back-to-back
+    calls (rotating over S sets), after `warm` untimed calls; HIP events on
+    the current stream.  Returns microseconds per call.  The long warm-up
+    matters after the idle gaps of the single-call latency loop: with 20
+    warm-up calls the conversion-heavy stores measured up to 7% slower."""
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        call(i % S)
+    torch.cuda.synchronize()
+    out = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            call(i % S)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out.append(e0.elapsed_time(e1) * 1e3 / n)
+    return statistics.median(out)
+
+
 def bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh, n=50):
     """The fused FP8 store with scales computed in the kernel (per token and
     per token-head) on the FP8 workload's inputs, rotated like the main step."""
@@ -306,16 +328,7 @@ def bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh, n=50):
             if st:
                 raise kv.KVStoreError(st, "kvstore_fp8_paged_dynamic")
 
-        for i in range(5):
-            call(i % S)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(torch.cuda.current_stream())
-        for i in range(n):
-            call(i % S)
-        e1.record(torch.cuda.current_stream())
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / n
+        us = time_calls(torch, call, S, n)
         T = c4.num_tokens
         b = 2 * T * 2 * R + T * 4 + 2 * T * R + 2 * T * G * 4
         out["fp8_dynamic_" + ("per_head" if per_head else "per_token")] = {
@@ -338,16 +351,7 @@ def bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh, n=50):
         if st:
             raise kv.KVStoreError(st, "kvstore_fp8_paged_e5m2")
 
-    for i in range(5):
-        call_e5m2(i % S)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(torch.cuda.current_stream())
-    for i in range(n):
-        call_e5m2(i % S)
-    e1.record(torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / n
+    us = time_calls(torch, call_e5m2, S, n)
     b = c4.algorithmic_bytes()
     out["fp8_e5m2"] = {
         "workload": "fused FP8 paged store into e5m2 caches (16384 tok, 8x128 bf16, int32, "
@@ -377,16 +381,7 @@ def bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh, n=100):
         if st:
             raise kv.KVStoreError(st, "kvstore_copy")
 
-    for i in range(5):
-        call(i % S)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(torch.cuda.current_stream())
-    for i in range(n):
-        call(i % S)
-    e1.record(torch.cuda.current_stream())
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / n
+    us = time_calls(torch, call, S, n)
     T = c3.num_tokens
     b = 2 * T * R * 2 + T * 4
     st, _, _ = kv.kvstore_check_error(sh)
@@ -475,7 +470,7 @@ def bench_wide_strided(kv, torch, dev, kvgen, to_dev, S=16, n=50):
     """Wide strided copy (8192 tokens, 1x576 fp16 = 1152 B rows read at a
     1280 B row stride, int64, 2^19 slots): average launch time over S
     disjoint input/index sets (about 600 MB per cycle, above the last-level
-    cache)."""
+    cache), median of three windows."""
     c5 = kvgen.workload(5)
     sets = kvgen.disjoint_index_sets(c5, S)
     k = [to_dev(c5.k)]
@@ -497,16 +492,7 @@ def bench_wide_strided(kv, torch, dev, kvgen, to_dev, S=16, n=50):
         if st:
             raise kv.KVStoreError(st, "kvstore_copy")
 
-    for i in range(S):
-        call(i % S)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(n):
-        call(i % S)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / n
+    us = time_calls(torch, call, S, n)
     st, _, _ = kv.kvstore_check_error(sh)
     assert st == kv.OK
     b = c5.algorithmic_bytes()
