@@ -205,12 +205,13 @@ def main():
     fp8_us = fp8_ms_total * 1e3 / K
     value = (b3 + b4) / (ms_per_step * 1e-3) / 1e9
 
-    decode = tiny = None
+    decode = tiny = fp8_decode = None
     if not args.no_decode:
         decode = bench_decode(kv, torch, dev, kvgen, to_dev, 2,
                               "decode copy (256 tok, 8x128 bf16, int64, 2^20 slots)")
         tiny = bench_decode(kv, torch, dev, kvgen, to_dev, 1,
                             "tiny copy (16 tok, 2x64 bf16, int32, 256 slots)")
+        fp8_decode = bench_fp8_decode(kv, torch, dev, kvgen, to_dev)
 
     next_rows = None
     if not args.no_next:
@@ -274,6 +275,7 @@ def main():
         "breakdown": breakdown,
         "decode_copy": decode,
         "tiny_copy": tiny,
+        "fp8_decode": fp8_decode,
         "wide_strided_copy": wide,
         "next_rows": next_rows,
         "cpu_baseline": cpu,
@@ -464,6 +466,72 @@ def bench_decode(kv, torch, dev, kvgen, to_dev, n_workload, label):
             "us_single_call_median": round(statistics.median(lat), 3),
             "us_per_call_graph_replay": round(graph_us, 3),
             "bytes": c2.algorithmic_bytes()}
+
+
+def bench_fp8_decode(kv, torch, dev, kvgen, to_dev, T=256):
+    """The fused FP8 paged store at decode size (256 tokens, 8x128 bf16,
+    int32, page 64, 2^21 slots, inverse scales 1/2.5 and 1/1.7): per-call
+    time back to back, single-call latency, and per call when 16 calls
+    captured in one HIP graph are replayed, over 16 disjoint index sets."""
+    c = kvgen.workload(4, tokens=T)
+    S = 16
+    sets = kvgen.disjoint_index_sets(c, S)
+    k = to_dev(c.k)
+    v = to_dev(c.v)
+    idx = [to_dev(a) for a in sets]
+    ik = to_dev(np.array([c.inv_k_bits], dtype=np.uint32).view(np.float32))
+    iv = to_dev(np.array([c.inv_v_bits], dtype=np.uint32).view(np.float32))
+    H, D, P = c.num_heads, c.head_dim, c.page_size
+    R = H * D
+    kc = torch.full((c.slots, R), 0xFF, dtype=torch.uint8, device=dev)
+    vc = torch.full_like(kc, 0xFF)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    def call(s, on=None):
+        st = kv.kvstore_fp8_paged(k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                                  idx[s].data_ptr(), kv.IDX_I32, 1, kv.SRC_BF16, H, D,
+                                  c.in_stride_bytes, 2 * D, c.in_stride_bytes, 2 * D, P * R, R, D,
+                                  P * R, R, D, c.num_tokens, c.slots, P, ik.data_ptr(),
+                                  iv.data_ptr(), sh if on is None else on)
+        if st:
+            raise kv.KVStoreError(st, "kvstore_fp8_paged")
+
+    b2b_us = time_calls(torch, call, S, n=400, reps=1, warm=200)
+    lat = []
+    for i in range(200):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call(i % S)
+        b.record(stream)
+        b.synchronize()
+        lat.append(a.elapsed_time(b) * 1e3)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for s in range(S):
+            call(s, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    reps = 25
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / (reps * S)
+    del g
+    st, _, _ = kv.kvstore_check_error(sh)
+    assert st == kv.OK
+    del kc, vc
+    return {"workload": "fused FP8 paged store at decode size (256 tok, 8x128 bf16, int32, "
+                        "page 64, 2^21 slots)",
+            "us_per_call_back_to_back": round(b2b_us, 3),
+            "us_single_call_median": round(statistics.median(lat), 3),
+            "us_per_call_graph_replay": round(graph_us, 3),
+            "bytes": c.algorithmic_bytes()}
 
 
 def bench_wide_strided(kv, torch, dev, kvgen, to_dev, S=16, n=50):
