@@ -102,7 +102,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(uint8_t* row) {
   return __builtin_amdgcn_make_buffer_rsrc(row, 0, 0x7FFFFFFF, 0x00020000);
 }
 
-
 // ---------------------------------------------------------------------------
 // Scatter copy.
 // ---------------------------------------------------------------------------
@@ -491,7 +490,6 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
     }
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // Fused e4m3fn quantise + paged store with dynamic scales.
