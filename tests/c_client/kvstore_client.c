@@ -6,6 +6,9 @@
  *   kvstore_client gpu        stores through every entry point into hipMalloc'd
  *                             buffers on the current device and compares every
  *                             byte with the CPU oracle (oracle/liboracle.so)
+ *   kvstore_client latency    per-call time of decode-size stores issued from C
+ *                             (256 tokens of 8 x 128 bf16): back to back, and
+ *                             replayed from a captured HIP graph
  *
  * Exit status 0 when every check passed; each failed check prints a line.
  * The oracle is test infrastructure: this program is a test.
@@ -425,15 +428,97 @@ static void gpu(void) {
   HIP_OK(hipStreamDestroy(s));
 }
 
+/* ------------------------------------------------------------------------ */
+/* latency: decode-size calls issued from C                                  */
+/* ------------------------------------------------------------------------ */
+
+static double elapsed_us(hipEvent_t a, hipEvent_t b, int calls) {
+  float ms = 0.0f;
+  HIP_OK(hipEventElapsedTime(&ms, a, b));
+  return ms * 1000.0 / calls;
+}
+
+static void latency(void) {
+  /* 256 tokens of 2 KiB rows, 16 disjoint index sets over 2^20 slots */
+  const int64_t T = 256, row = 2048, slots = 1 << 20, H = 8, D = 128, P = 64;
+  const int S = 16, N = 2000;
+  g_state = 7ull;
+  uint8_t* h = (uint8_t*)malloc((size_t)(T * row));
+  fill_random(h, (size_t)(T * row));
+  void *k = dev_copy_of(h, (size_t)(T * row)), *v = dev_copy_of(h, (size_t)(T * row));
+  int32_t* ix = (int32_t*)malloc((size_t)(S * T) * sizeof *ix);
+  random_slots(ix, S * T, slots);
+  int32_t* dix = (int32_t*)dev_copy_of(ix, (size_t)(S * T) * sizeof *ix);
+  void *kc = dev_sentinel((size_t)(slots * row)), *vc = dev_sentinel((size_t)(slots * row));
+  const float inv[2] = {0.4f, 1.0f / 1.7f};
+  float* dinv = (float*)dev_copy_of(inv, sizeof inv);
+  hipStream_t s;
+  HIP_OK(hipStreamCreate(&s));
+  hipEvent_t a, b;
+  HIP_OK(hipEventCreate(&a));
+  HIP_OK(hipEventCreate(&b));
+  for (int op = 0; op < 2; ++op) {
+    const char* name = op ? "kvstore_fp8_paged" : "kvstore_copy";
+    /* fp8: the same 2 KiB input rows as 8 x 128 bf16, into 1 KiB FP8 slots */
+#define CALL(i, st)                                                                          \
+  (op ? kvstore_fp8_paged(k, v, kc, vc, dix + ((i) % S) * T, KVSTORE_IDX_I32, 1,               \
+                          KVSTORE_SRC_BF16, (int32_t)H, (int32_t)D, row, 2 * D, row, 2 * D,   \
+                          P * H * D, H * D, D, P * H * D, H * D, D, (uint32_t)T, slots, P,    \
+                          dinv, dinv + 1, st)                                                 \
+      : kvstore_copy(k, v, kc, vc, dix + ((i) % S) * T, KVSTORE_IDX_I32, 1, row, row, row,     \
+                     row, (uint32_t)T, slots, st))
+    for (int i = 0; i < 200; ++i) EXPECT(CALL(i, s) == KVSTORE_OK, "%s warm-up", name);
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipEventRecord(a, s));
+    for (int i = 0; i < N; ++i) CALL(i, s);
+    HIP_OK(hipEventRecord(b, s));
+    HIP_OK(hipEventSynchronize(b));
+    const double b2b = elapsed_us(a, b, N);
+    hipGraph_t g;
+    hipGraphExec_t ge;
+    HIP_OK(hipStreamBeginCapture(s, hipStreamCaptureModeGlobal));
+    for (int i = 0; i < S; ++i) CALL(i, s);
+    HIP_OK(hipStreamEndCapture(s, &g));
+    HIP_OK(hipGraphInstantiate(&ge, g, NULL, NULL, 0));
+    for (int r = 0; r < 20; ++r) HIP_OK(hipGraphLaunch(ge, s));
+    HIP_OK(hipStreamSynchronize(s));
+    HIP_OK(hipEventRecord(a, s));
+    for (int r = 0; r < N / S; ++r) HIP_OK(hipGraphLaunch(ge, s));
+    HIP_OK(hipEventRecord(b, s));
+    HIP_OK(hipEventSynchronize(b));
+    const double graph = elapsed_us(a, b, (N / S) * S);
+    HIP_OK(hipGraphExecDestroy(ge));
+    HIP_OK(hipGraphDestroy(g));
+#undef CALL
+    printf("[c-client] %s, 256 tokens, from C: %.3f us/call back to back, %.3f us/call "
+           "replayed from a graph\n", name, b2b, graph);
+  }
+  int64_t fb;
+  uint64_t bc;
+  EXPECT(kvstore_check_error(s, &fb, &bc) == KVSTORE_OK, "latency: flag set");
+  HIP_OK(hipStreamDestroy(s));
+  HIP_OK(hipFree(k));
+  HIP_OK(hipFree(v));
+  HIP_OK(hipFree(dix));
+  HIP_OK(hipFree(kc));
+  HIP_OK(hipFree(vc));
+  HIP_OK(hipFree(dinv));
+  free(h);
+  free(ix);
+}
+
 int main(int argc, char** argv) {
-  if (argc != 2 || (strcmp(argv[1], "validate") != 0 && strcmp(argv[1], "gpu") != 0)) {
-    fprintf(stderr, "usage: %s validate|gpu\n", argv[0]);
+  if (argc != 2 || (strcmp(argv[1], "validate") != 0 && strcmp(argv[1], "gpu") != 0 &&
+                    strcmp(argv[1], "latency") != 0)) {
+    fprintf(stderr, "usage: %s validate|gpu|latency\n", argv[0]);
     return 64;
   }
   if (strcmp(argv[1], "validate") == 0)
     validate();
-  else
+  else if (strcmp(argv[1], "gpu") == 0)
     gpu();
+  else
+    latency();
   printf("[c-client] %s: %d failure(s)\n", argv[1], g_failures);
   return g_failures ? 1 : 0;
 }
