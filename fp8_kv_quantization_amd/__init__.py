@@ -1,8 +1,10 @@
 """Python binding of libkvstore, the MI355X (gfx950) KV-cache store.
 
 Argument marshalling only: every step of a store runs in the HIP kernels of
-``libkvstore.so`` (built from ``csrc/kvstore.hip``).  There is no fallback: if
-the library is not built, importing this package raises.
+``libkvstore.so`` (built from ``csrc/kvstore.hip``); the functions named like
+the C ABI come from the CPython extension ``_kvstore_py`` (``csrc/kvstore_py.c``),
+which converts Python ints and calls the library.  There is no fallback: if
+either is not built, importing this package raises.
 
 Low level (same names and arguments as the C ABI in ``include/kvstore.h``;
 pointers are ints, strides in bytes unless stated):
@@ -36,7 +38,6 @@ Tensor level (torch tensors on the GPU; the current stream is used):
 """
 from __future__ import annotations
 
-import ctypes as C
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -59,113 +60,26 @@ SCALE_PER_TOKEN_HEAD = 1
 EXPORTED = ("kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_e5m2",
             "kvstore_fp8_paged_dynamic", "kvstore_check_error", "kvstore_strerror")
 
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
+
+# ---------------------------------------------------------------------------
+# C ABI, one to one: the same names and arguments as include/kvstore.h
+# (pointers as ints, None for NULL; strides in bytes unless stated; the
+# trailing stream is optional).  Each returns the C status; the error check
+# returns (status, first_bad_token, bad_count).
+# ---------------------------------------------------------------------------
+from ._kvstore_py import (kvstore_check_error, kvstore_copy,  # noqa: E402,F401
+                          kvstore_fp8_paged, kvstore_fp8_paged_dynamic,
+                          kvstore_fp8_paged_e5m2, kvstore_strerror)
+
 
 class KVStoreError(RuntimeError):
     def __init__(self, status: int, what: str = ""):
         self.status = status
         super().__init__(f"{what}: {kvstore_strerror(status)} (status {status})" if what
                          else f"{kvstore_strerror(status)} (status {status})")
-
-
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(
-            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'`")
-    lib = C.CDLL(LIB_PATH)
-    vp, i64, i32, u32 = C.c_void_p, C.c_int64, C.c_int, C.c_uint32
-    lib.kvstore_copy.argtypes = [vp, vp, vp, vp, vp, i32, i64, i64, i64, i64, i64, u32, i64, vp]
-    lib.kvstore_copy.restype = i32
-    lib.kvstore_fp8_paged.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, C.c_int32, C.c_int32,
-                                      i64, i64, i64, i64, i64, i64, i64, i64, i64, i64, u32, i64,
-                                      i64, vp, vp, vp]
-    lib.kvstore_fp8_paged.restype = i32
-    lib.kvstore_fp8_paged_e5m2.argtypes = lib.kvstore_fp8_paged.argtypes
-    lib.kvstore_fp8_paged_e5m2.restype = i32
-    lib.kvstore_fp8_paged_dynamic.argtypes = [vp, vp, vp, vp, vp, i32, i64, i32, C.c_int32,
-                                              C.c_int32, i64, i64, i64, i64, i64, i64, i64, i64,
-                                              i64, i64, vp, vp, i32, i64, i64, i64, i64, i64, i64,
-                                              u32, i64, i64, vp]
-    lib.kvstore_fp8_paged_dynamic.restype = i32
-    lib.kvstore_check_error.argtypes = [vp, C.POINTER(C.c_int64), C.POINTER(C.c_uint64)]
-    lib.kvstore_check_error.restype = i32
-    lib.kvstore_strerror.argtypes = [i32]
-    lib.kvstore_strerror.restype = C.c_char_p
-    return lib
-
-
-_lib = _load()
-
-
-# ---------------------------------------------------------------------------
-# C ABI, one to one
-# ---------------------------------------------------------------------------
-
-def kvstore_copy(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, row_bytes,
-                 k_stride_bytes, v_stride_bytes, cache_stride_bytes, batch, size_limit,
-                 stream=None) -> int:
-    return _lib.kvstore_copy(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, row_bytes,
-                             k_stride_bytes, v_stride_bytes, cache_stride_bytes, batch,
-                             size_limit, stream)
-
-
-def kvstore_fp8_paged(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype,
-                      num_heads, head_dim, k_stride_token_bytes, k_stride_head_bytes,
-                      v_stride_token_bytes, v_stride_head_bytes, kc_stride_page_bytes,
-                      kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
-                      vc_stride_offset_bytes, vc_stride_head_bytes, batch, size_limit,
-                      page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream=None) -> int:
-    return _lib.kvstore_fp8_paged(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride,
-                                  src_dtype, num_heads, head_dim, k_stride_token_bytes,
-                                  k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
-                                  kc_stride_page_bytes, kc_stride_offset_bytes,
-                                  kc_stride_head_bytes, vc_stride_page_bytes,
-                                  vc_stride_offset_bytes, vc_stride_head_bytes, batch,
-                                  size_limit, page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream)
-
-
-def kvstore_fp8_paged_e5m2(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype,
-                           num_heads, head_dim, k_stride_token_bytes, k_stride_head_bytes,
-                           v_stride_token_bytes, v_stride_head_bytes, kc_stride_page_bytes,
-                           kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
-                           vc_stride_offset_bytes, vc_stride_head_bytes, batch, size_limit,
-                           page_size, inv_k_scale_ptr, inv_v_scale_ptr, stream=None) -> int:
-    return _lib.kvstore_fp8_paged_e5m2(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride,
-                                       src_dtype, num_heads, head_dim, k_stride_token_bytes,
-                                       k_stride_head_bytes, v_stride_token_bytes,
-                                       v_stride_head_bytes, kc_stride_page_bytes,
-                                       kc_stride_offset_bytes, kc_stride_head_bytes,
-                                       vc_stride_page_bytes, vc_stride_offset_bytes,
-                                       vc_stride_head_bytes, batch, size_limit, page_size,
-                                       inv_k_scale_ptr, inv_v_scale_ptr, stream)
-
-
-def kvstore_fp8_paged_dynamic(k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype,
-                              num_heads, head_dim, k_stride_token_bytes, k_stride_head_bytes,
-                              v_stride_token_bytes, v_stride_head_bytes, kc_stride_page_bytes,
-                              kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
-                              vc_stride_offset_bytes, vc_stride_head_bytes, k_scale_cache,
-                              v_scale_cache, granularity, ks_stride_page_bytes,
-                              ks_stride_offset_bytes, ks_stride_head_bytes, vs_stride_page_bytes,
-                              vs_stride_offset_bytes, vs_stride_head_bytes, batch, size_limit,
-                              page_size, stream=None) -> int:
-    return _lib.kvstore_fp8_paged_dynamic(
-        k, v, k_cache, v_cache, indices, idx_dtype, idx_stride, src_dtype, num_heads, head_dim,
-        k_stride_token_bytes, k_stride_head_bytes, v_stride_token_bytes, v_stride_head_bytes,
-        kc_stride_page_bytes, kc_stride_offset_bytes, kc_stride_head_bytes, vc_stride_page_bytes,
-        vc_stride_offset_bytes, vc_stride_head_bytes, k_scale_cache, v_scale_cache, granularity,
-        ks_stride_page_bytes, ks_stride_offset_bytes, ks_stride_head_bytes, vs_stride_page_bytes,
-        vs_stride_offset_bytes, vs_stride_head_bytes, batch, size_limit, page_size, stream)
-
-
-def kvstore_check_error(stream=None):
-    fb = C.c_int64(0)
-    bc = C.c_uint64(0)
-    st = _lib.kvstore_check_error(stream, C.byref(fb), C.byref(bc))
-    return st, fb.value, bc.value
-
-
-def kvstore_strerror(status: int) -> str:
-    return _lib.kvstore_strerror(status).decode()
 
 
 # ---------------------------------------------------------------------------

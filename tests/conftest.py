@@ -15,10 +15,12 @@ def pytest_configure(config):
 
 
 def pytest_sessionstart(session):
-    # Build the HIP library only when nothing is built (a fresh checkout):
-    # tests load what is built and never rebuild an existing library.
+    # Build the HIP library and its binding only when they are not built (a
+    # fresh checkout): tests load what is built and never rebuild them.
     lib = os.path.join(ROOT, "fp8_kv_quantization_amd", "libkvstore.so")
-    if not os.path.exists(lib):
+    pkg = os.path.join(ROOT, "fp8_kv_quantization_amd")
+    has_binding = any(f.startswith("_kvstore_py") and f.endswith(".so") for f in os.listdir(pkg))
+    if not os.path.exists(lib) or not has_binding:
         path = os.path.join(ROOT, "fp8_kv_quantization_amd", "_build.py")
         spec = importlib.util.spec_from_file_location("_kvstore_build", path)
         mod = importlib.util.module_from_spec(spec)

@@ -56,6 +56,27 @@ def test_library_exports_every_declared_symbol(kv):
 def test_binding_names_match_the_abi(kv):
     for name in declared_functions():
         assert callable(getattr(kv, name))
+        # the compiled binding, not a Python stand-in
+        assert type(getattr(kv, name)).__name__ == "builtin_function_or_method", name
+
+
+def test_binding_links_the_in_tree_library(kv):
+    from fp8_kv_quantization_amd import _kvstore_py
+    out = subprocess.run(["ldd", _kvstore_py.__file__], capture_output=True, text=True,
+                         check=True).stdout
+    assert "libkvstore.so" in out and "not found" not in out.split("libkvstore.so")[1].split("\n")[0]
+
+
+def test_binding_argument_errors(kv):
+    with pytest.raises(TypeError):
+        kv.kvstore_copy(0, 0, 0)                       # too few arguments
+    with pytest.raises(TypeError):
+        kv.kvstore_copy(*([0] * 15))                   # too many
+    with pytest.raises(OverflowError):
+        kv.kvstore_copy(0, 0, 0, 0, 0, 0, 1, 16, 16, 16, 16, 1 << 32, 1)   # batch > 32 bits
+    with pytest.raises(TypeError):
+        kv.kvstore_copy("k", 0, 0, 0, 0, 0, 1, 16, 16, 16, 16, 1, 1)      # not an int
+    assert kv.kvstore_copy(0, 0, 0, 0, 0, 0, 1, 16, 16, 16, 16, 0, 1, None) == kv.OK
 
 
 def test_strerror_texts(kv):

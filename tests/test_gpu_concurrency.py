@@ -2,7 +2,7 @@
 
 The library keeps no per-call host state beyond a per-device cache of one
 device attribute, and the device flag is updated with atomics, so calls may
-be issued concurrently.  Four threads (the ctypes calls release the GIL) each
+be issued concurrently.  Four threads (the binding releases the GIL) each
 own a stream and their own caches and issue interleaved copy, FP8 and
 dynamic-scale stores; afterwards every cache must match the oracle and the
 shared flag must hold the smallest out-of-range token and the count over all
