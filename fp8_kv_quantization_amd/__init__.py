@@ -14,6 +14,7 @@ pointers are ints, strides in bytes unless stated):
     kvstore_fp8_paged_e5m2(...) -> status
     kvstore_fp8_paged_dynamic(...) -> status
     kvstore_check_error(stream) -> (status, first_bad_token, bad_count)
+    kvstore_take_error(out_ptr, stream) -> status   (graph-capturable, no sync)
     kvstore_strerror(status) -> str
 
 Tensor level (torch tensors on the GPU; the current stream is used):
@@ -58,7 +59,8 @@ SCALE_PER_TOKEN = 0
 SCALE_PER_TOKEN_HEAD = 1
 
 EXPORTED = ("kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_e5m2",
-            "kvstore_fp8_paged_dynamic", "kvstore_check_error", "kvstore_strerror")
+            "kvstore_fp8_paged_dynamic", "kvstore_check_error", "kvstore_take_error",
+            "kvstore_strerror")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -72,7 +74,7 @@ if not os.path.exists(LIB_PATH):
 # ---------------------------------------------------------------------------
 from ._kvstore_py import (kvstore_check_error, kvstore_copy,  # noqa: E402,F401
                           kvstore_fp8_paged, kvstore_fp8_paged_dynamic,
-                          kvstore_fp8_paged_e5m2, kvstore_strerror)
+                          kvstore_fp8_paged_e5m2, kvstore_strerror, kvstore_take_error)
 
 
 class KVStoreError(RuntimeError):
@@ -303,6 +305,20 @@ def store_kv_fp8_paged_dynamic(k, v, k_cache, v_cache, cache_loc, k_scale_cache,
             vss[0], vss[1], vss[2], T, limit, page_size, _stream_handle(stream, dev))
     if st != OK:
         raise KVStoreError(st, "kvstore_fp8_paged_dynamic")
+
+
+def take_error(out, stream=None):
+    """Enqueue the graph-capturable error take: `out`, an int64 GPU tensor of
+    two elements, receives (first_bad_token or -1, bad_count) when the stream
+    reaches the call, and the flag is cleared.  Does not synchronise."""
+    torch = _torch()
+    dev = _device_of(out)
+    if out.dtype != torch.int64 or out.numel() != 2 or not out.is_contiguous():
+        raise TypeError("out must be a contiguous int64 GPU tensor of two elements")
+    with torch.cuda.device(dev):
+        st = kvstore_take_error(out.data_ptr(), _stream_handle(stream, dev))
+    if st != OK:
+        raise KVStoreError(st, "kvstore_take_error")
 
 
 def check_error(stream=None, device=None):

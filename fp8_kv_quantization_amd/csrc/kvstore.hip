@@ -64,6 +64,15 @@ __device__ __forceinline__ void report_bad_token(uint32_t token) {
   atomicAdd(&g_kvstore_error.bad_count, 1ull);
 }
 
+// Takes the flag into out[0] (smallest bad token, or -1) and out[1] (count),
+// leaving it cleared.  One thread.
+__global__ void kvstore_take_error_kernel(int64_t* out) {
+  const unsigned long long first = atomicExch(&g_kvstore_error.first_bad, ~0ull);
+  const unsigned long long count = atomicExch(&g_kvstore_error.bad_count, 0ull);
+  out[0] = first == ~0ull ? -1 : (int64_t)first;
+  out[1] = (int64_t)count;
+}
+
 __device__ __forceinline__ uint32_t wave_uniform(uint32_t x) {
   return __builtin_amdgcn_readfirstlane(x);
 }
@@ -1158,6 +1167,12 @@ int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* 
   if (first_bad_token) *first_bad_token = h.bad_count ? (int64_t)h.first_bad : -1;
   if (bad_count) *bad_count = h.bad_count;
   return h.bad_count ? KVSTORE_ERR_OOB : KVSTORE_OK;
+}
+
+int kvstore_take_error(int64_t* out_device, hipStream_t stream) {
+  if (!out_device) return KVSTORE_ERR_NULL;
+  if (!aligned(out_device, 8)) return KVSTORE_ERR_ALIGN;
+  return launch(kvstore_take_error_kernel, dim3(1), dim3(1), 0, stream, out_device);
 }
 
 const char* kvstore_strerror(int status) {

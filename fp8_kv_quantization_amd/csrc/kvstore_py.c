@@ -178,6 +178,20 @@ static PyObject* py_kvstore_check_error(PyObject* self, PyObject* const* a, Py_s
   return Py_BuildValue("(iLK)", st, (long long)first_bad, (unsigned long long)count);
 }
 
+static PyObject* py_kvstore_take_error(PyObject* self, PyObject* const* a, Py_ssize_t n) {
+  (void)self;
+  void* out;
+  hipStream_t s;
+  if (!check_nargs("kvstore_take_error", n, 1) || !to_ptr(a[0], &out) ||
+      !stream_arg(a, n, 1, &s))
+    return NULL;
+  int st;
+  Py_BEGIN_ALLOW_THREADS
+  st = kvstore_take_error((int64_t*)out, s);
+  Py_END_ALLOW_THREADS
+  return PyLong_FromLong(st);
+}
+
 static PyObject* py_kvstore_strerror(PyObject* self, PyObject* const* a, Py_ssize_t n) {
   (void)self;
   int status;
@@ -201,6 +215,8 @@ static PyMethodDef methods[] = {
      "See include/kvstore.h."},
     {"kvstore_check_error", FASTCALL(py_kvstore_check_error), METH_FASTCALL,
      "Returns (status, first_bad_token, bad_count)."},
+    {"kvstore_take_error", FASTCALL(py_kvstore_take_error), METH_FASTCALL,
+     "See include/kvstore.h."},
     {"kvstore_strerror", FASTCALL(py_kvstore_strerror), METH_FASTCALL, "Status text."},
     {NULL, NULL, 0, NULL}};
 

@@ -240,6 +240,21 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
  */
 int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* bad_count);
 
+/*
+ * Graph-capturable form of kvstore_check_error: enqueues on `stream` a
+ * one-thread kernel that takes the current device's error flag into
+ * `out_device` and clears it, without waiting.  out_device points to two
+ * int64 in device memory (8-byte aligned): out_device[0] receives the smallest
+ * rejected token position since the last take or check, or -1; out_device[1]
+ * the number of rejected tokens.  Stores issued earlier on the same stream are
+ * included; the caller reads the two values whenever it synchronises (for
+ * example after replaying a graph that captured stores and this call).  The
+ * flag is shared by all streams of the device, as for kvstore_check_error.
+ * Returns KVSTORE_OK, KVSTORE_ERR_NULL, KVSTORE_ERR_ALIGN or KVSTORE_ERR_HIP
+ * (nothing launched).
+ */
+int kvstore_take_error(int64_t* out_device, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char* kvstore_strerror(int status);
 

@@ -173,6 +173,10 @@ static void validate(void) {
   EXPECT(dyn_call(KVSTORE_SCALE_PER_TOKEN_HEAD, 8, 128, sc, 32, 2) == KVSTORE_ERR_ALIGN,
          "dynamic scale head stride not a multiple of 4");
 
+  /* graph-capturable error take */
+  EXPECT(kvstore_take_error(NULL, 0) == KVSTORE_ERR_NULL, "take_error null");
+  EXPECT(kvstore_take_error((int64_t*)A4, 0) == KVSTORE_ERR_ALIGN, "take_error misaligned");
+
   /* status text */
   for (int s = KVSTORE_ERR_OOB; s <= KVSTORE_OK; ++s) {
     const char* t = kvstore_strerror(s);

@@ -40,7 +40,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["kvstore_copy", "kvstore_fp8_paged", "kvstore_fp8_paged_e5m2",
-         "kvstore_fp8_paged_dynamic", "kvstore_check_error", "kvstore_strerror"])
+         "kvstore_fp8_paged_dynamic", "kvstore_check_error", "kvstore_take_error",
+         "kvstore_strerror"])
 
 
 def test_library_exports_every_declared_symbol(kv):
@@ -292,3 +293,8 @@ def test_dynamic_valid_arguments_reach_the_runtime(kv):
                      v_stride_token_bytes=2048, k_stride_head_bytes=96, v_stride_head_bytes=96,
                      kc_stride_head_bytes=48, vc_stride_head_bytes=48) == kv.ERR_HIP
     assert _dyn_call(kv, batch=0, k=0) == kv.OK
+
+
+def test_take_error_rejects_before_launch(kv):
+    assert kv.kvstore_take_error(None) == kv.ERR_NULL
+    assert kv.kvstore_take_error(A + 4) == kv.ERR_ALIGN

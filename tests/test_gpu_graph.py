@@ -11,7 +11,8 @@ Each test captures calls once and replays the graph three times.  Between
 replays, eager work on the same stream overwrites the inputs, indices and
 scales with a new seeded case and resets the caches to the 0xFF sentinel; after
 each replay every byte of every output buffer is compared with the oracle run
-on that case, and the error flag with the oracle's count.
+on that case, and the error flag with the oracle's count.  The last two tests
+cover kvstore_take_error, the error read that can sit inside a graph.
 """
 import dataclasses
 
@@ -22,7 +23,7 @@ import torch
 import fp8_kv_quantization_amd as kv
 import kvgen
 import oracle
-from tests._gpu import assert_cache_equal, check_flag, sentinel_cache, stream, to_dev
+from tests._gpu import DEV, assert_cache_equal, check_flag, sentinel_cache, stream, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -240,3 +241,61 @@ def test_graph_step_copy_then_fp8():
         assert_cache_equal(vc, ovc, f"copy v_cache replay {i}")
         assert_cache_equal(fkc, ofk, f"fp8 k_cache replay {i}")
         assert_cache_equal(fvc, ofv, f"fp8 v_cache replay {i}")
+
+
+def test_take_error_eager_collects_and_clears():
+    """kvstore_take_error after two stores with bad tokens: the smallest bad
+    token and the total count land in the device buffer, and the flag is
+    cleared (a later check finds nothing)."""
+    c = kvgen.workload(1, tokens=200, slots=1024)
+    c.indices = c.indices.copy()
+    c.indices[[9, 150]] = c.slots
+    c2 = kvgen.workload(1, tokens=200, slots=1024, seed=77)
+    c2.indices = c2.indices.copy()
+    c2.indices[4] = -1
+    kc = sentinel_cache(c.slots, c.row_bytes)
+    vc = sentinel_cache(c.slots, c.row_bytes)
+    out = torch.full((2,), 12345, dtype=torch.int64, device=DEV)
+    for case in (c, c2):
+        k, v, idx = to_dev(case.k), to_dev(case.v), to_dev(case.indices)
+        assert kv.kvstore_copy(k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                               idx.data_ptr(), kv.IDX_I32, 1, case.row_bytes, case.in_stride_bytes,
+                               case.in_stride_bytes, case.row_bytes, case.num_tokens, case.slots,
+                               stream()) == kv.OK
+    kv.take_error(out)
+    torch.cuda.synchronize()
+    assert out.tolist() == [4, 3]
+    assert check_flag() == (kv.OK, -1, 0)
+    kv.take_error(out)                      # nothing since: -1, 0
+    torch.cuda.synchronize()
+    assert out.tolist() == [-1, 0]
+
+
+def test_take_error_inside_a_graph():
+    """A graph holding a store and the error take: each replay reports the
+    bad tokens of that replay only, with no host synchronisation in the graph."""
+    c = kvgen.workload(3, tokens=1000, slots=1 << 13, seed=31)
+    k, v, idx = to_dev(c.k), to_dev(c.v), to_dev(c.indices)
+    good = idx.clone()
+    kc = sentinel_cache(c.slots, c.row_bytes)
+    vc = sentinel_cache(c.slots, c.row_bytes)
+    out = torch.zeros(2, dtype=torch.int64, device=DEV)
+
+    def store():
+        return kv.kvstore_copy(k.data_ptr(), v.data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                               idx.data_ptr(), kv.IDX_I32, 1, c.row_bytes, c.in_stride_bytes,
+                               c.in_stride_bytes, c.row_bytes, c.num_tokens, c.slots, stream())
+
+    def take():
+        return kv.kvstore_take_error(out.data_ptr(), stream())
+
+    g = _capture([store, take])
+    for i, bad in enumerate(([], [333], [], [12, 999, 500])):
+        _say(f"graph take_error replay {i} bad={bad}")
+        idx.copy_(good)
+        for t in bad:
+            idx[t] = c.slots + t
+        out.fill_(12345)
+        _replay(g)
+        assert out.tolist() == ([min(bad), len(bad)] if bad else [-1, 0])
+        assert check_flag() == (kv.OK, -1, 0)
