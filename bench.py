@@ -219,6 +219,7 @@ def main():
         next_rows.update(bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh))
 
     wide = bench_wide_strided(kv, torch, dev, kvgen, to_dev)
+    plain = None if args.no_next else bench_plain_kernels(torch, dev, b3, c4, S)
 
     traffic = stored_traffic()
     roofline = {
@@ -278,6 +279,7 @@ def main():
         "fp8_decode": fp8_decode,
         "wide_strided_copy": wide,
         "next_rows": next_rows,
+        "plain_kernels_same_bytes": plain,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -303,6 +305,38 @@ def time_calls(torch, call, S, n=50, reps=3, warm=500):
         torch.cuda.synchronize()
         out.append(e0.elapsed_time(e1) * 1e3 / n)
     return statistics.median(out)
+
+
+def bench_plain_kernels(torch, dev, copy_bytes, c4, S, n=50):
+    """Same-GPU reference points for the two kernels of the step: torch's own
+    device copy moving the prefill copy's byte count (contiguous, no index,
+    no scatter), and torch's own bf16 -> float8_e4m3fn cast over the FP8
+    workload's element count (contiguous in and out, no scale, no paging),
+    each rotated over S buffer sets like the step."""
+    out = {}
+    half = copy_bytes // 2
+    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(s) for s in range(S)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
+    us = time_calls(torch, lambda s: dst[s].copy_(src[s]), S, n=n)
+    out["torch_copy"] = {"bytes": 2 * half, "avg_launch_us": round(us, 3),
+                         "GB/s": round(2 * half / (us * 1e-6) / 1e9, 1),
+                         "frac_of_peak": round(2 * half / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del src, dst
+    elems = 2 * c4.num_tokens * c4.num_heads * c4.head_dim
+    try:
+        src = [torch.randn(elems, device=dev).to(torch.bfloat16) for _ in range(S)]
+        dst = [torch.empty(elems, dtype=torch.float8_e4m3fn, device=dev) for _ in range(S)]
+        us = time_calls(torch, lambda s: dst[s].copy_(src[s]), S, n=n)
+        nbytes = 3 * elems
+        out["torch_cast_bf16_to_e4m3fn"] = {
+            "bytes": nbytes, "avg_launch_us": round(us, 3),
+            "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del src, dst
+    except (RuntimeError, TypeError) as e:   # cast not available in this torch build
+        out["torch_cast_bf16_to_e4m3fn"] = {"error": str(e)[:200]}
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh, n=50):

@@ -649,6 +649,9 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
   uint8_t* scales = is_v ? d.v_scales + page * d.vs_stride_page + off * d.vs_stride_offset
                          : d.k_scales + page * d.ks_stride_page + off * d.ks_stride_offset;
   const int64_t s_head = is_v ? d.vs_stride_head : d.ks_stride_head;
+  // per-head scales need gph to be a power of two (checked on the host): the
+  // head of group g is g >> log2(gph)
+  const uint32_t gsh = __builtin_ctz(gph);
 #pragma unroll
   for (int j = 0; j < kPasses; ++j) {
     const uint32_t g = j * (2u * kWave) + lane;
@@ -666,10 +669,10 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
     if (!d.per_head) {
       if (g == 0) *reinterpret_cast<float*>(scales) = sa;
     } else if (gph > kWave) {
-      if (lane == 0) *reinterpret_cast<float*>(scales + (g / gph) * s_head) = sa;
+      if (lane == 0) *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa;
     } else if ((lane & (gph - 1)) == 0) {
-      *reinterpret_cast<float*>(scales + (g / gph) * s_head) = sa;
-      if (has_b) *reinterpret_cast<float*>(scales + ((g + kWave) / gph) * s_head) = sb;
+      *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa;
+      if (has_b) *reinterpret_cast<float*>(scales + ((g + kWave) >> gsh) * s_head) = sb;
     }
   }
 }
