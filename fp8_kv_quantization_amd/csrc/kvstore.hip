@@ -10,7 +10,8 @@
 //                          caches, and with scales computed per token or per
 //                          token and head (kvstore_fp8_paged_e5m2 / _dynamic).
 //
-// Both are pure data movement, bound by HBM bandwidth; no MFMA and no LDS.
+// Both are pure data movement, bound by HBM bandwidth: no MFMA, and no LDS
+// traffic (the copy allocates LDS only to cap its residency).
 // Design points for CDNA4:
 //   * one 64-lane wave per (token, slice of the row) -- for fp8, per (token,
 //     K or V); each lane loads 16 B per access (dwordx4), so one wave access

@@ -417,6 +417,46 @@ static void gpu_dynamic(hipStream_t s, int gran) {
   free(ovs);
 }
 
+static void gpu_take_error(hipStream_t s) {
+  /* 64 tokens of 256-byte rows into 128 slots, tokens 40, 3 and 9 out of
+   * range: the take reports (3, 3) in device memory and clears the flag. */
+  const int64_t T = 64, row = 256, slots = 128;
+  uint8_t* k = (uint8_t*)malloc((size_t)(T * row));
+  int32_t* ix = (int32_t*)malloc((size_t)T * sizeof *ix);
+  fill_random(k, (size_t)(T * row));
+  random_slots(ix, T, slots);
+  ix[40] = (int32_t)slots;
+  ix[3] = (int32_t)(slots + 7);
+  ix[9] = -1;
+  void* dk = dev_copy_of(k, (size_t)(T * row));
+  void* dix = dev_copy_of(ix, (size_t)T * sizeof *ix);
+  void *dkc = dev_sentinel((size_t)(slots * row)), *dvc = dev_sentinel((size_t)(slots * row));
+  int64_t* dout = (int64_t*)dev_sentinel(2 * sizeof(int64_t));
+  printf("[c-client] take_error T=%lld\n", (long long)T);
+  fflush(stdout);
+  EXPECT(kvstore_copy(dk, dk, dkc, dvc, dix, KVSTORE_IDX_I32, 1, row, row, row, row, (uint32_t)T,
+                      slots, s) == KVSTORE_OK, "take_error: store");
+  EXPECT(kvstore_take_error(dout, s) == KVSTORE_OK, "take_error: launch");
+  HIP_OK(hipStreamSynchronize(s));
+  int64_t out[2] = {0, 0};
+  HIP_OK(hipMemcpy(out, dout, sizeof out, hipMemcpyDeviceToHost));
+  EXPECT(out[0] == 3 && out[1] == 3, "take_error: got (%lld, %lld), want (3, 3)",
+         (long long)out[0], (long long)out[1]);
+  expect_flag(s, -1, 0, "after take_error");
+  EXPECT(kvstore_take_error(dout, s) == KVSTORE_OK, "take_error: second launch");
+  HIP_OK(hipStreamSynchronize(s));
+  HIP_OK(hipMemcpy(out, dout, sizeof out, hipMemcpyDeviceToHost));
+  EXPECT(out[0] == -1 && out[1] == 0, "take_error on a clear flag: got (%lld, %lld)",
+         (long long)out[0], (long long)out[1]);
+  HIP_OK(hipFree(dk));
+  HIP_OK(hipFree(dix));
+  HIP_OK(hipFree(dkc));
+  HIP_OK(hipFree(dvc));
+  HIP_OK(hipFree(dout));
+  free(k);
+  free(ix);
+}
+
 static void gpu(void) {
   g_state = 20240611ull;
   hipStream_t s;
@@ -428,6 +468,7 @@ static void gpu(void) {
   gpu_fp8(s, 1, KVSTORE_SRC_BF16);
   gpu_dynamic(s, KVSTORE_SCALE_PER_TOKEN);
   gpu_dynamic(s, KVSTORE_SCALE_PER_TOKEN_HEAD);
+  gpu_take_error(s);
   HIP_OK(hipStreamSynchronize(s));
   HIP_OK(hipStreamDestroy(s));
 }
