@@ -13,20 +13,20 @@
 // Both are pure data movement, bound by HBM bandwidth: no MFMA, and no LDS
 // traffic (the copy allocates LDS only to cap its residency).
 // Design points for CDNA4:
-//   * one 64-lane wave per (token, slice of the row) -- for fp8, per (token,
-//     K or V); each lane loads 16 B per access (dwordx4), so one wave access
+//   * one 64-lane wave per (token, K or V, slice of the row); each lane
+//     loads 16 B per access (dwordx4), so one wave access
 //     covers 1 KiB of consecutive row bytes; copy rows or pointers aligned
 //     only to 8 or 4 bytes use 8- or 4-byte lanes, and copy rows that need at
 //     most 32 lanes are packed several to a wave;
-//   * every load of a wave (K and V, all its 1 KiB chunks) is issued before the
+//   * every load of a wave (all its 1 KiB chunks) is issued before the
 //     index is needed: the source address does not depend on the index, so the
 //     index fetch overlaps the data fetch instead of preceding it;
 //   * the row base addresses are wave-uniform 64-bit values (scalar registers)
 //     and the per-lane offset is a 32-bit vector register;
 //   * copy: cache rows are written with non-temporal stores, and residency is
-//     capped to about 32 KiB of loads in flight per CU (8 waves of 2 KiB rows;
-//     see copy_waves_per_cu): the rows land at scattered slots, and fewer
-//     concurrent write streams measured faster;
+//     capped to about 28 KiB of loads in flight per CU (14 waves of 2 KiB
+//     rows; see copy_waves_per_cu): the rows land at scattered slots, and
+//     fewer concurrent write streams measured faster;
 //   * fp8: the quantised rows are written with the sc1 cache policy through a
 //     per-row buffer descriptor, at full occupancy (the conversion needs the
 //     latency hiding);
@@ -49,7 +49,7 @@ constexpr int kWavesPerBlock = 2;             // fp8 kernels
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
 constexpr int kCopyWavesPerBlock = 2;         // copy kernel
 constexpr int kCopyBlockThreads = kWave * kCopyWavesPerBlock;
-constexpr int kMaxChunksPerWave = 4;          // 4 KiB of K + 4 KiB of V in flight per wave
+constexpr int kMaxChunksPerWave = 4;          // 4 KiB of K or of V in flight per wave
 
 // ---------------------------------------------------------------------------
 // Device error flag (replaces the page's device assert on a bad slot id).
@@ -131,9 +131,13 @@ struct CopyParams {
   uint32_t token_base;  // first token of this launch
 };
 
-// One row per wave.  Grid: x = ceil(batch / kCopyWavesPerBlock) blocks of
-// kCopyWavesPerBlock waves, one wave per token; y = slices of the row, kChunks
-// chunks of 64 * VW bytes each.
+// One row slice of K or of V per wave.  Grid: x = ceil(batch / kCopyWavesPerBlock)
+// blocks of kCopyWavesPerBlock waves, one wave per token; y = slices of the
+// row, kChunks chunks of 64 * VW bytes each; z = 2: K (0) or V (1).  Blocks
+// are dispatched x first, so a launch moves its K rows, then its V rows; K and
+// V in separate waves of half the bytes let the residency cap be set in
+// finer steps (2 KiB-row copy: 14 waves of 2 KiB per CU, 1.5% faster than
+// 8 waves moving 2 KiB of K and 2 KiB of V each).
 template <int VW, int kChunks, typename IdxT>
 __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const CopyParams p) {
   typedef typename LaneVec<VW>::type T;
@@ -143,36 +147,30 @@ __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const C
   if (i >= p.batch) return;
   const uint32_t token = p.token_base + i;
   const uint32_t slice = blockIdx.y;
+  const bool is_v = blockIdx.z != 0;
 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
 
-  const uint8_t* ks = p.k + (int64_t)token * p.k_stride;
-  const uint8_t* vs = p.v + (int64_t)token * p.v_stride;
+  const uint8_t* src =
+      is_v ? p.v + (int64_t)token * p.v_stride : p.k + (int64_t)token * p.k_stride;
   const uint32_t col0 = slice * (kChunks * kChunk) + lane * VW;
 
-  T kr[kChunks], vr[kChunks];
+  T r[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const uint32_t col = col0 + c * kChunk;
-    if (col < p.row_bytes) {
-      kr[c] = loadv<VW>(ks, col);
-      vr[c] = loadv<VW>(vs, col);
-    }
+    if (col < p.row_bytes) r[c] = loadv<VW>(src, col);
   }
 
   if (loc < 0 || loc >= p.size_limit) {
-    if (lane == 0 && slice == 0) report_bad_token(token);
+    if (lane == 0 && slice == 0 && !is_v) report_bad_token(token);
     return;
   }
-  uint8_t* kd = p.k_cache + loc * p.cache_stride;
-  uint8_t* vd = p.v_cache + loc * p.cache_stride;
+  uint8_t* dst = (is_v ? p.v_cache : p.k_cache) + loc * p.cache_stride;
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const uint32_t col = col0 + c * kChunk;
-    if (col < p.row_bytes) {
-      storev<VW>(kd, col, kr[c]);
-      storev<VW>(vd, col, vr[c]);
-    }
+    if (col < p.row_bytes) storev<VW>(dst, col, r[c]);
   }
 }
 
@@ -702,13 +700,14 @@ int launch(void (*kernel)(Args...), dim3 grid, dim3 block, uint32_t lds_bytes,
              : KVSTORE_ERR_HIP;
 }
 
-// Resident copy waves per CU: enough for about 32 KiB of loads in flight per
+// Resident copy waves per CU: enough for about 28 KiB of loads in flight per
 // CU, at least 8 and at most 32 (every wave slot).  The copy writes rows at
 // scattered slots; with every wave slot filled the scattered write streams of
-// the 2 KiB-row prefill copy measured ~5% slower than with 6-10 waves per CU
-// (8 waves x 4 KiB), while rows that move fewer bytes per wave need more waves
-// to keep the loads in flight (1152-byte rows: 14 waves, 4.6% faster than 8).
-constexpr int64_t kCopyLoadBytesPerCU = 32768;
+// the 2 KiB-row prefill copy measured ~5% slower, and with 16-20 KiB in
+// flight (8-10 waves of 2 KiB) the loads stall it by ~12%; 14 waves of 2 KiB
+// measured best.  Rows that move fewer bytes per wave get more waves
+// (1152-byte rows: 25).
+constexpr int64_t kCopyLoadBytesPerCU = 28 * 1024;
 inline int64_t copy_waves_per_cu(int64_t load_bytes_per_wave) {
   const int64_t w = (kCopyLoadBytesPerCU + load_bytes_per_wave / 2) / load_bytes_per_wave;
   return w < 8 ? 8 : w > 32 ? 32 : w;
@@ -772,13 +771,13 @@ int launch_copy_vw(const CopyParams& p, hipStream_t stream) {
   const int per_wave = (int)(chunks < kMaxChunksPerWave ? chunks : kMaxChunksPerWave);
   const int64_t slices = ceil_div(chunks, per_wave);
   if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
-  const dim3 grid((uint32_t)ceil_div(p.batch, kCopyWavesPerBlock), (uint32_t)slices);
+  const dim3 grid((uint32_t)ceil_div(p.batch, kCopyWavesPerBlock), (uint32_t)slices, 2);
   // The kernel uses no LDS; the dynamic allocation only caps residency (tuned
   // for 16-byte lanes, where a wave has the most bytes in flight).  A wave
-  // loads the K and V bytes of its row slice.
+  // loads one row slice of K or of V.
   const int64_t lds = VW == 16 ? lds_per_cu() : 0;
   const int64_t slice_bytes = (int64_t)per_wave * kChunk;
-  const int64_t wave_bytes = 2 * (p.row_bytes < slice_bytes ? (int64_t)p.row_bytes : slice_bytes);
+  const int64_t wave_bytes = p.row_bytes < slice_bytes ? (int64_t)p.row_bytes : slice_bytes;
   const int64_t blocks_per_cu = copy_waves_per_cu(wave_bytes) / kCopyWavesPerBlock;
   const uint32_t lds_bytes = lds > 0 ? (uint32_t)(lds / blocks_per_cu) : 0;
   switch (per_wave) {
