@@ -41,7 +41,9 @@
  * kernel does not check them at all.  Here a token whose index is outside
  * [0, size_limit) is skipped (neither its K nor its V row is written, every
  * other token is) and recorded in a per-device error flag, read and cleared
- * by kvstore_check_error.  Store calls report only argument errors.
+ * by kvstore_check_error (which synchronises) or, in stream order and inside
+ * a captured graph, by kvstore_take_error.  Store calls report only argument
+ * errors.
  *
  * Indices must be unique within one call: two tokens naming the same slot
  * race, and which one lands is undefined (as on the pages).
