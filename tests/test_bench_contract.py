@@ -1,0 +1,75 @@
+"""bench.py's output contract: the one JSON line, its fields and their
+consistency; the multi-GPU refusal; the use of stored counter figures only
+while they belong to the current kernel source."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import bench
+import kvgen
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_stored_traffic_belongs_to_the_current_source(monkeypatch):
+    t = bench.stored_traffic()
+    assert t is not None, "the counter summary was taken on another kernel source"
+    b3 = kvgen.workload(3).algorithmic_bytes()
+    b4 = kvgen.workload(4).algorithmic_bytes()
+    # read and written bytes within a few percent of the algorithmic ones
+    assert 0.98 < (t["copy_fetch_bytes"] + t["copy_write_bytes"]) / b3 < 1.05
+    assert 0.98 < (t["fp8_fetch_bytes"] + t["fp8_write_bytes"]) / b4 < 1.05
+    monkeypatch.setattr(bench, "source_sha", lambda: "0" * 64)
+    assert bench.stored_traffic() is None
+
+
+def test_stored_traffic_absent_summary(monkeypatch, tmp_path):
+    monkeypatch.setattr(bench, "PMC_SUMMARY", str(tmp_path / "missing.md"))
+    assert bench.stored_traffic() is None
+
+
+@pytest.mark.gpu
+def test_bench_line_contract():
+    print("[gpu-case] bench.py --steps 3 --warmup 1 --no-decode --no-next --cpu-reps 1", flush=True)
+    r = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
+                        "--warmup", "1", "--no-decode", "--no-next", "--cpu-reps", "1"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, r.stdout
+    d = json.loads(lines[0])
+    for key, typ in (("metric", str), ("value", float), ("unit", str), ("n_gpus", int),
+                     ("steps", int), ("warmup", int), ("ms_per_step", float),
+                     ("higher_is_better", bool), ("scaling", str), ("dtype", str),
+                     ("data", str), ("config", dict), ("roofline", dict),
+                     ("cpu_baseline", dict)):
+        assert isinstance(d[key], typ), key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["higher_is_better"] is True and d["scaling"] in ("weak", "strong")
+    assert d["vs_baseline"] is None
+    assert "workload" in d["config"] and "model" not in d["config"]
+    b3 = kvgen.workload(3).algorithmic_bytes()
+    b4 = kvgen.workload(4).algorithmic_bytes()
+    assert d["config"]["bytes_per_step"] == b3 + b4
+    # value is the step's bytes over the step time
+    assert abs(d["value"] - (b3 + b4) / (d["ms_per_step"] * 1e-3) / 1e9) / d["value"] < 0.01
+    rf = d["roofline"]
+    assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
+    assert rf["algorithmic_bytes"] == b3
+    assert abs(rf["achieved"] - b3 / (rf["avg_launch_us"] * 1e-6) / 1e9) / rf["achieved"] < 0.01
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert 0.0 < rf["frac"] < 1.0
+    assert rf["traffic"] is None or 0.98 < rf["traffic"] / b3 < 1.05
+    cb = d["cpu_baseline"]
+    assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
