@@ -310,9 +310,10 @@ def time_calls(torch, call, S, n=50, reps=3, warm=500):
 def bench_plain_kernels(torch, dev, copy_bytes, c4, S, n=50):
     """Same-GPU reference points for the two kernels of the step: torch's own
     device copy moving the prefill copy's byte count (contiguous, no index,
-    no scatter), and torch's own bf16 -> float8_e4m3fn cast over the FP8
+    no scatter), torch's own bf16 -> float8_e4m3fn cast over the FP8
     workload's element count (contiguous in and out, no scale, no paging),
-    each rotated over S buffer sets like the step."""
+    and the hand-written plain kernels of bench_plain.hip, each rotated over
+    S buffer sets like the step."""
     out = {}
     half = copy_bytes // 2
     src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(s) for s in range(S)]
@@ -335,6 +336,55 @@ def bench_plain_kernels(torch, dev, copy_bytes, c4, S, n=50):
         del src, dst
     except (RuntimeError, TypeError) as e:   # cast not available in this torch build
         out["torch_cast_bf16_to_e4m3fn"] = {"error": str(e)[:200]}
+    torch.cuda.empty_cache()
+    out.update(bench_hand_plain(torch, dev, copy_bytes, elems, S, n))
+    return out
+
+
+def bench_hand_plain(torch, dev, copy_bytes, fp8_elems, S, n=50):
+    """The hand-written plain kernels of bench_plain.hip (built next to this
+    file by __graft_entry__.build()): a contiguous copy of the prefill copy's
+    byte count, and the FP8 store's per-wave shape (2 KiB read, 1 KiB
+    written) over its wave count, with no index, scatter or conversion.
+    Empty if the library is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_plain.so")
+    if not os.path.exists(path):
+        return {}
+    lib = ctypes.CDLL(path)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
+    sh = torch.cuda.current_stream().cuda_stream
+    out = {}
+    half = copy_bytes // 2 // 16 * 16
+    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(s + 1) for s in range(S)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
+
+    def copy(s):
+        if lib.bench_plain_copy(src[s].data_ptr(), dst[s].data_ptr(), half, sh) != 0:
+            raise RuntimeError("bench_plain_copy failed")
+
+    us = time_calls(torch, copy, S, n=n)
+    out["hand_plain_copy"] = {"bytes": 2 * half, "avg_launch_us": round(us, 3),
+                              "GB/s": round(2 * half / (us * 1e-6) / 1e9, 1),
+                              "frac_of_peak": round(2 * half / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del src, dst
+    waves = fp8_elems // 1024                   # one wave per 1024 elements (2 KiB of bf16)
+    src = [torch.empty(waves * 2048, dtype=torch.uint8, device=dev).fill_(s + 1) for s in range(S)]
+    dst = [torch.empty(waves * 1024, dtype=torch.uint8, device=dev) for _ in range(S)]
+
+    def shape(s):
+        if lib.bench_plain_read2_write1(src[s].data_ptr(), dst[s].data_ptr(), waves, sh) != 0:
+            raise RuntimeError("bench_plain_read2_write1 failed")
+
+    us = time_calls(torch, shape, S, n=n)
+    nbytes = waves * 3072
+    out["hand_plain_read2k_write1k"] = {"bytes": nbytes, "waves": waves,
+                                        "avg_launch_us": round(us, 3),
+                                        "GB/s": round(nbytes / (us * 1e-6) / 1e9, 1),
+                                        "frac_of_peak": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    del src, dst
     torch.cuda.empty_cache()
     return out
 

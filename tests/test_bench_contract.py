@@ -78,3 +78,48 @@ def test_bench_line_contract():
     assert rf["traffic"] is None or 0.98 < rf["traffic"] / b3 < 1.05
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
+
+
+def test_plain_reference_library_exports():
+    import ctypes
+    path = os.path.join(ROOT, "bench_plain.so")
+    if not os.path.exists(path):
+        pytest.skip("bench_plain.so not built")
+    lib = ctypes.CDLL(path)
+    for name in ("bench_plain_copy", "bench_plain_read2_write1"):
+        assert hasattr(lib, name), name
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
+    # argument errors return before any launch (no GPU needed)
+    assert lib.bench_plain_copy(None, None, 16, None) == -1
+    assert lib.bench_plain_copy(16, 32, 15, None) == -1
+    assert lib.bench_plain_copy(8, 32, 16, None) == -1
+    assert lib.bench_plain_read2_write1(16, 32, 0, None) == -1
+
+
+@pytest.mark.gpu
+def test_plain_reference_kernels_move_the_right_bytes():
+    import ctypes
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "bench_plain.so"))
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
+    dev = torch.device("cuda:0")
+    sh = torch.cuda.current_stream().cuda_stream
+    g = torch.Generator().manual_seed(5)
+    for nbytes in (16, 4096, 4112, 1 << 20, (1 << 20) + 4080):
+        print(f"[gpu-case] plain copy {nbytes} B", flush=True)
+        src = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g).to(dev)
+        dst = torch.zeros(nbytes + 4096, dtype=torch.uint8, device=dev)
+        assert lib.bench_plain_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:nbytes], src) and int(dst[nbytes:].sum()) == 0
+    for waves in (1, 2, 3, 1001):
+        print(f"[gpu-case] plain read2/write1 {waves} waves", flush=True)
+        src = torch.randint(0, 256, (waves, 2, 1024), dtype=torch.uint8, generator=g).to(dev)
+        dst = torch.zeros(waves + 4, 1024, dtype=torch.uint8, device=dev)
+        assert lib.bench_plain_read2_write1(src.data_ptr(), dst.data_ptr(), waves, sh) == 0
+        torch.cuda.synchronize()
+        assert torch.equal(dst[:waves], src[:, 0] ^ src[:, 1]) and int(dst[waves:].sum()) == 0
