@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sets", type=int, default=8, help="disjoint input/index sets rotated over")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--cpu-reps", type=int, default=21,
+                    help="oracle runs of one full step (about 0.55 s each on one core)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also launch a plain device copy of this size (counter calibration)")
     ap.add_argument("--no-decode", action="store_true")
@@ -676,8 +677,9 @@ def cpu_baseline(c3, c4, reps):
     t = statistics.median(times)
     b = c3.algorithmic_bytes() + c4.algorithmic_bytes()
     return {"value": round(b / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one full step (prefill copy 32768 tok + fused FP8 paged 16384 tok, "
-                      f"set 0) into full-size host caches; median of {reps} runs",
+            "sample": f"{reps} runs of one full step (prefill copy 32768 tok + fused FP8 paged "
+                      f"16384 tok, set 0) into full-size host caches, {sum(times):.1f} s of "
+                      f"CPU work; median run",
             "seconds_per_step": round(t, 4),
             "host_cpus": os.cpu_count()}
 
