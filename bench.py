@@ -206,14 +206,6 @@ def main():
     fp8_us = fp8_ms_total * 1e3 / K
     value = (b3 + b4) / (ms_per_step * 1e-3) / 1e9
 
-    decode = tiny = fp8_decode = None
-    if not args.no_decode:
-        decode = bench_decode(kv, torch, dev, kvgen, to_dev, 2,
-                              "decode copy (256 tok, 8x128 bf16, int64, 2^20 slots)")
-        tiny = bench_decode(kv, torch, dev, kvgen, to_dev, 1,
-                            "tiny copy (16 tok, 2x64 bf16, int32, 256 slots)")
-        fp8_decode = bench_fp8_decode(kv, torch, dev, kvgen, to_dev)
-
     next_rows = None
     if not args.no_next:
         next_rows = bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh)
@@ -221,6 +213,17 @@ def main():
 
     wide = bench_wide_strided(kv, torch, dev, kvgen, to_dev)
     plain = None if args.no_next else bench_plain_kernels(torch, dev, b3, c4, S)
+
+    # Launch-bound decode-size figures last: the idle gaps of their
+    # single-call latency loop leave the GPU slow to return to full speed for
+    # the bandwidth-bound timings above.
+    decode = tiny = fp8_decode = None
+    if not args.no_decode:
+        decode = bench_decode(kv, torch, dev, kvgen, to_dev, 2,
+                              "decode copy (256 tok, 8x128 bf16, int64, 2^20 slots)")
+        tiny = bench_decode(kv, torch, dev, kvgen, to_dev, 1,
+                            "tiny copy (16 tok, 2x64 bf16, int32, 256 slots)")
+        fp8_decode = bench_fp8_decode(kv, torch, dev, kvgen, to_dev)
 
     traffic = stored_traffic()
     roofline = {
