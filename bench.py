@@ -70,10 +70,14 @@ def stored_traffic():
     if vals.get("kernel_source_sha256") != source_sha():
         return None
     try:
-        return {k: float(vals[k]) for k in ("copy_fetch_bytes", "copy_write_bytes",
-                                            "fp8_fetch_bytes", "fp8_write_bytes")}
+        out = {k: float(vals[k]) for k in ("copy_fetch_bytes", "copy_write_bytes",
+                                           "fp8_fetch_bytes", "fp8_write_bytes")}
     except KeyError:
         return None
+    for k in ("wide_fetch_bytes", "wide_write_bytes"):
+        if k in vals:
+            out[k] = float(vals[k])
+    return out
 
 
 def main():
@@ -212,6 +216,9 @@ def main():
         next_rows.update(bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh))
 
     wide = bench_wide_strided(kv, torch, dev, kvgen, to_dev)
+    traffic = stored_traffic()
+    if traffic is not None and "wide_fetch_bytes" in traffic:
+        wide["traffic"] = int(traffic["wide_fetch_bytes"] + traffic["wide_write_bytes"])
     plain = None if args.no_next else bench_plain_kernels(torch, dev, b3, c4, S)
 
     # Launch-bound decode-size figures last: the idle gaps of their
@@ -225,7 +232,6 @@ def main():
                             "tiny copy (16 tok, 2x64 bf16, int32, 256 slots)")
         fp8_decode = bench_fp8_decode(kv, torch, dev, kvgen, to_dev)
 
-    traffic = stored_traffic()
     roofline = {
         "bound": "hbm",
         "kernel": "kvstore_copy_kernel<16, 2, int> (prefill copy)",
