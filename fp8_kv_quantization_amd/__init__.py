@@ -27,15 +27,17 @@ Tensor level (torch tensors on the GPU; the current stream is used):
         sglang "trtllm_fp8_kv_kernel.py" fused_fp8_set_kv_buffer: k/v
         [T, H, D] or [T, H*D] bf16/fp16; caches uint8 (e4m3fn bytes) or
         float8_e4m3fn, flat [slots, H, D] or paged [pages, page_size, H, D];
-        inverse scales as fp32 device tensors (one element) or None.  Caches
-        of dtype float8_e5m2 (or fp8_format="e5m2") get e5m2 codes; uint8 and
-        float8_e4m3fn caches get e4m3fn codes.
+        inverse scales as fp32 device tensors (one element) or None.  uint8
+        and float8_e4m3fn caches get e4m3fn codes, float8_e5m2 caches e5m2
+        codes; any other cache dtype (the fnuz formats among them) raises
+        TypeError, as do K and V caches of different dtypes.
     store_kv_fp8_paged_dynamic(k, v, k_cache, v_cache, cache_loc,
                                k_scale_cache, v_scale_cache, per_head=False,
                                page_size=16, size_limit=None)
         the same store with scales computed per token (or per token and head)
         and written as fp32 into scale caches shaped [slots] / [slots, H]
-        (flat) or [pages, page_size] / [pages, page_size, H] (paged).
+        (flat) or [pages, page_size] / [pages, page_size, H] (paged); the
+        caches hold e4m3fn codes (uint8 or float8_e4m3fn).
 """
 from __future__ import annotations
 
@@ -164,6 +166,30 @@ def store_kv(k, v, k_cache, v_cache, indices, size_limit=None, stream=None) -> N
         raise KVStoreError(st, "kvstore_copy")
 
 
+def _fp8_format(k_cache, v_cache, fp8_format=None, allowed=("e4m3fn", "e5m2")):
+    """The FP8 code format the two caches receive.  Both caches must share
+    one dtype.  e4m3fn codes go into uint8 or float8_e4m3fn caches, e5m2
+    codes into float8_e5m2 caches; fp8_format defaults to the one the cache
+    dtype names (e4m3fn for uint8).  Anything else, the fnuz formats (another
+    exponent bias and NaN encoding) included, raises TypeError."""
+    torch = _torch()
+    if k_cache.dtype != v_cache.dtype:
+        raise TypeError(f"k_cache and v_cache must share one dtype ({k_cache.dtype} != "
+                        f"{v_cache.dtype})")
+    dt = k_cache.dtype
+    holds = {"e4m3fn": (torch.uint8, torch.float8_e4m3fn), "e5m2": (torch.float8_e5m2,)}
+    if fp8_format is None:
+        fp8_format = "e5m2" if dt == torch.float8_e5m2 else "e4m3fn"
+    if fp8_format not in holds:
+        raise ValueError(f"unknown fp8_format {fp8_format!r}")
+    if fp8_format not in allowed:
+        raise TypeError(f"this store writes {' or '.join(allowed)} codes, not {fp8_format}")
+    if dt not in holds[fp8_format]:
+        raise TypeError(f"a {dt} cache cannot hold {fp8_format} codes: e4m3fn codes go into "
+                        "uint8 or float8_e4m3fn caches, e5m2 codes into float8_e5m2 caches")
+    return fp8_format
+
+
 def _cache_strides(cache, page_size):
     """(num_heads, head_dim, slots, (page, offset, head) byte strides) of a
     flat [slots, H, D] or paged [pages, page_size, H, D] byte cache."""
@@ -210,10 +236,7 @@ def store_kv_fp8_paged(k, v, k_cache, v_cache, cache_loc, page_size=16, inv_k_sc
     the device; None means unscaled).  fp8_format "e4m3fn" or "e5m2"; by
     default e5m2 for float8_e5m2 caches, else e4m3fn."""
     torch = _torch()
-    if fp8_format is None:
-        fp8_format = "e5m2" if k_cache.dtype == torch.float8_e5m2 else "e4m3fn"
-    if fp8_format not in ("e4m3fn", "e5m2"):
-        raise ValueError(f"unknown fp8_format {fp8_format!r}")
+    fp8_format = _fp8_format(k_cache, v_cache, fp8_format)
     entry = kvstore_fp8_paged_e5m2 if fp8_format == "e5m2" else kvstore_fp8_paged
     dev = _device_of(k, v, k_cache, v_cache, cache_loc, inv_k_scale, inv_v_scale)
     if k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16:
@@ -274,6 +297,7 @@ def store_kv_fp8_paged_dynamic(k, v, k_cache, v_cache, cache_loc, k_scale_cache,
     """Fused e4m3fn quantise + paged store with per-token (or per token and
     head) scales computed in the kernel and written to the scale caches."""
     torch = _torch()
+    _fp8_format(k_cache, v_cache, "e4m3fn", allowed=("e4m3fn",))
     dev = _device_of(k, v, k_cache, v_cache, cache_loc, k_scale_cache, v_scale_cache)
     if k.dtype == torch.bfloat16 and v.dtype == torch.bfloat16:
         src = SRC_BF16
