@@ -24,7 +24,7 @@
 //   * the row base addresses are wave-uniform 64-bit values (scalar registers)
 //     and the per-lane offset is a 32-bit vector register;
 //   * copy: cache rows are written with non-temporal stores, and residency is
-//     capped to about 28 KiB of loads in flight per CU (14 waves of 2 KiB
+//     capped to about 24 KiB of loads in flight per CU (12 waves of 2 KiB
 //     rows; see copy_waves_per_cu): the rows land at scattered slots, and
 //     fewer concurrent write streams measured faster;
 //   * fp8: the quantised rows are written with the sc1 cache policy through a
@@ -37,6 +37,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "kvstore.h"
 
@@ -53,26 +54,41 @@ constexpr int kMaxChunksPerWave = 4;          // 4 KiB of K or of V in flight pe
 
 // ---------------------------------------------------------------------------
 // Device error flag (replaces the page's device assert on a bad slot id).
+// One 64-bit word per device: bits 0-31 hold the smallest rejected token
+// (0xFFFFFFFF if none; token positions stay below 2^32 - 1), bits 32-63 the
+// number of rejected tokens, saturating at 2^32 - 1.  Every report is one
+// compare-and-swap and every take one exchange, so a take always sees the
+// count and the smallest token of the same set of reports.
 // ---------------------------------------------------------------------------
-struct DeviceError {
-  unsigned long long first_bad;  // smallest rejected token, ~0 if none
-  unsigned long long bad_count;
-};
-__device__ DeviceError g_kvstore_error = {~0ull, 0ull};
+constexpr unsigned long long kFlagClear = 0xFFFFFFFFull;
+__device__ unsigned long long g_kvstore_error = kFlagClear;
+
+__device__ __forceinline__ unsigned long long flag_with(unsigned long long f, uint32_t token) {
+  const uint32_t first = (uint32_t)f < token ? (uint32_t)f : token;
+  const uint32_t count = (uint32_t)(f >> 32);
+  return ((unsigned long long)(count == 0xFFFFFFFFu ? count : count + 1u) << 32) | first;
+}
 
 __device__ __forceinline__ void report_bad_token(uint32_t token) {
-  atomicMin(&g_kvstore_error.first_bad, (unsigned long long)token);
-  atomicAdd(&g_kvstore_error.bad_count, 1ull);
+  unsigned long long seen = kFlagClear;
+  for (;;) {
+    const unsigned long long prev = atomicCAS(&g_kvstore_error, seen, flag_with(seen, token));
+    if (prev == seen) return;
+    seen = prev;
+  }
 }
 
 // Takes the flag into out[0] (smallest bad token, or -1) and out[1] (count),
 // leaving it cleared.  One thread.
 __global__ void kvstore_take_error_kernel(int64_t* out) {
-  const unsigned long long first = atomicExch(&g_kvstore_error.first_bad, ~0ull);
-  const unsigned long long count = atomicExch(&g_kvstore_error.bad_count, 0ull);
-  out[0] = first == ~0ull ? -1 : (int64_t)first;
+  const unsigned long long f = atomicExch(&g_kvstore_error, kFlagClear);
+  const uint32_t count = (uint32_t)(f >> 32);
+  out[0] = count ? (int64_t)(uint32_t)f : -1;
   out[1] = (int64_t)count;
 }
+
+// Where kvstore_check_error takes the flag to, per device; one check at a time.
+__device__ int64_t g_kvstore_taken[2];
 
 __device__ __forceinline__ uint32_t wave_uniform(uint32_t x) {
   return __builtin_amdgcn_readfirstlane(x);
@@ -136,8 +152,8 @@ struct CopyParams {
 // row, kChunks chunks of 64 * VW bytes each; z = 2: K (0) or V (1).  Blocks
 // are dispatched x first, so a launch moves its K rows, then its V rows; K and
 // V in separate waves of half the bytes let the residency cap be set in
-// finer steps (2 KiB-row copy: 14 waves of 2 KiB per CU, 1.5% faster than
-// 8 waves moving 2 KiB of K and 2 KiB of V each).
+// finer steps (2 KiB-row copy: 12 waves of 2 KiB per CU, 1.5% faster than
+// the best cap of waves moving 2 KiB of K and 2 KiB of V each).
 template <int VW, int kChunks, typename IdxT>
 __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const CopyParams p) {
   typedef typename LaneVec<VW>::type T;
@@ -510,7 +526,6 @@ struct Fp8DynParams {
   uint8_t* v_scales;
   int64_t ks_stride_page, ks_stride_offset, ks_stride_head;
   int64_t vs_stride_page, vs_stride_offset, vs_stride_head;
-  int32_t per_head;
 };
 
 // max |x| over the 8 source elements of one 16-byte vector; NaN elements are
@@ -532,6 +547,35 @@ __device__ __forceinline__ float amax8(u32x4 a) {
   return m;
 }
 
+// A magnitude |x| of a bf16 / fp16 element as its 15-bit pattern (sign
+// cleared), and back.  For values that are not NaN these patterns order like
+// the magnitudes, and the conversions are exact.
+template <bool kFp16>
+__device__ __forceinline__ float mag_to_float(uint32_t m) {
+  if constexpr (kFp16) return (float)__builtin_bit_cast(_Float16, (uint16_t)m);
+  else return __uint_as_float(m << 16);
+}
+template <bool kFp16>
+__device__ __forceinline__ uint32_t float_to_mag(float f) {
+  if constexpr (kFp16) return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)f);
+  else return __float_as_uint(f) >> 16;
+}
+
+// max |x| over the 8 elements of one 16-byte vector, as a magnitude pattern.
+// has_nan: some element of the lane may be NaN; then NaN elements are ignored
+// (fmaxf), else the patterns are compared directly, two per packed 16-bit max.
+template <bool kFp16>
+__device__ __forceinline__ uint32_t amax8_mag(u32x4 a, bool has_nan) {
+  if (has_nan) return float_to_mag<kFp16>(amax8<kFp16>(a));
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  const u16x2 m = __builtin_elementwise_max(
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.x & 0x7FFF7FFFu),
+                                __builtin_bit_cast(u16x2, a.y & 0x7FFF7FFFu)),
+      __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.z & 0x7FFF7FFFu),
+                                __builtin_bit_cast(u16x2, a.w & 0x7FFF7FFFu)));
+  return m.x > m.y ? m.x : m.y;
+}
+
 // One DPP step of a lane max: each lane takes the larger of its value and the
 // value of the lane that the row permutation kCtrl selects.
 template <int kCtrl>
@@ -540,13 +584,11 @@ __device__ __forceinline__ uint32_t dpp_max(uint32_t v) {
   return v > o ? v : o;
 }
 
-// Max over aligned groups of `lanes` lanes (a power of two <= 64), for
-// non-negative, non-NaN floats: their bit patterns order like their values, so
-// an unsigned max is exact.  Groups of up to 16 lanes reduce inside a DPP row
-// (quad swaps, then the half-row and row mirrors); a 32-lane group adds one
-// cross-row shuffle, and the whole wave combines its four rows with readlane.
-__device__ __forceinline__ float group_max(float x, uint32_t lanes) {
-  uint32_t v = __builtin_bit_cast(uint32_t, x);
+// Unsigned max over aligned groups of `lanes` lanes (a power of two <= 64).
+// Groups of up to 16 lanes reduce inside a DPP row (quad swaps, then the
+// half-row and row mirrors); a 32-lane group adds one cross-row shuffle, and
+// the whole wave combines its four rows with readlane.
+__device__ __forceinline__ uint32_t group_max(uint32_t v, uint32_t lanes) {
   if (lanes >= 2) v = dpp_max<0xB1>(v);    // quad_perm [1,0,3,2]: lane ^ 1
   if (lanes >= 4) v = dpp_max<0x4E>(v);    // quad_perm [2,3,0,1]: lane ^ 2
   if (lanes >= 8) v = dpp_max<0x141>(v);   // row_half_mirror: the other quad of 8
@@ -560,7 +602,7 @@ __device__ __forceinline__ float group_max(float x, uint32_t lanes) {
     const uint32_t o = (uint32_t)__shfl_xor((int)v, 16);
     v = v > o ? v : o;
   }
-  return __builtin_bit_cast(float, v);
+  return v;
 }
 
 // fp32 scale of a group, at least the smallest normal float.
@@ -571,11 +613,13 @@ __device__ __forceinline__ float dyn_scale(float amax) {
 // Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = 2: K (0) or
 // V (1).  The wave holds the tensor's whole row: kPasses passes of 1024
 // elements, as in the static store (lane l takes 8-element groups l and
-// l + 64 of each pass).  Per token, one scale covers the row.  Per head, with
-// gph = head_dim / 8 groups per head: for gph <= 64 each head lies wholly in
-// the first or the second group of its lanes, on gph aligned lanes; for
-// gph = 128 (head_dim 1024) a head is one whole pass.
-template <int kPasses, bool kFlat, bool kFp16, typename IdxT>
+// l + 64 of each pass).  kPerHead false: one scale covers the row.  Per head,
+// with gph = head_dim / 8 groups per head: for gph <= 64 each head lies
+// wholly in the first or the second group of its lanes, on gph aligned lanes;
+// for gph = 128 (head_dim 1024) a head is one whole pass.  Group maxima are
+// taken on the 15-bit magnitude patterns of the 16-bit inputs and converted
+// to fp32 once per group.
+template <int kPasses, bool kFlat, bool kFp16, bool kPerHead, typename IdxT>
 __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(const Fp8DynParams d) {
   const Fp8Params& p = d.base;
   const uint32_t lane = threadIdx.x % kWave;
@@ -608,22 +652,24 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
   }
   // Every lane takes part in the lane reductions below (groups past the row
   // hold zeros), so the bounds check comes after them.
-  float ma[kPasses], mb[kPasses];
+  bool nan[kPasses];
+  uint32_t ma[kPasses], mb[kPasses];
 #pragma unroll
   for (int j = 0; j < kPasses; ++j) {
-    ma[j] = amax8<kFp16>(a[j]);
-    mb[j] = amax8<kFp16>(b[j]);
+    nan[j] = any_nan16<kFp16>(a[j], b[j]);
+    ma[j] = amax8_mag<kFp16>(a[j], nan[j]);
+    mb[j] = amax8_mag<kFp16>(b[j], nan[j]);
   }
-  if (!d.per_head) {
-    float mx = 0.0f;
+  if constexpr (!kPerHead) {
+    uint32_t mx = 0;
 #pragma unroll
-    for (int j = 0; j < kPasses; ++j) mx = __builtin_fmaxf(mx, __builtin_fmaxf(ma[j], mb[j]));
+    for (int j = 0; j < kPasses; ++j) mx = max(mx, max(ma[j], mb[j]));
     mx = group_max(mx, kWave);
 #pragma unroll
     for (int j = 0; j < kPasses; ++j) ma[j] = mb[j] = mx;
   } else if (gph > kWave) {
 #pragma unroll
-    for (int j = 0; j < kPasses; ++j) ma[j] = mb[j] = group_max(__builtin_fmaxf(ma[j], mb[j]), kWave);
+    for (int j = 0; j < kPasses; ++j) ma[j] = mb[j] = group_max(max(ma[j], mb[j]), kWave);
   } else {
 #pragma unroll
     for (int j = 0; j < kPasses; ++j) {
@@ -656,16 +702,19 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
     const uint32_t g = j * (2u * kWave) + lane;
     if (g >= groups) continue;
     const bool has_b = g + kWave < groups;
-    const float sa = dyn_scale(ma[j]), sb = dyn_scale(mb[j]);
+    const float sa = dyn_scale(mag_to_float<kFp16>(ma[j]));
+    const float sb = dyn_scale(mag_to_float<kFp16>(mb[j]));
     const float ia = 1.0f / sa, ib = 1.0f / sb;
     // the inverses are finite and non-zero unless a group holds an infinity
-    const u32x4 q = quantize16<kFp16, false>(a[j], b[j], ia, ib, ia != 0.0f && ib != 0.0f);
+    const u32x4 q = (!nan[j] && ia != 0.0f && ib != 0.0f)
+                        ? quantize16_no_nan<kFp16, false>(a[j], b[j], ia, ib)
+                        : quantize16<kFp16, false>(a[j], b[j], ia, ib, false);
     store8_sc1(dst, da[j], u32x2{q.x, q.y});
     if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
     // One lane per group writes its scale: lane 0 of the wave per token; per
     // head, the first of each head's gph lanes (for gph = 128, lane 0 of the
     // pass), for the head of each of its two groups.
-    if (!d.per_head) {
+    if constexpr (!kPerHead) {
       if (g == 0) *reinterpret_cast<float*>(scales) = sa;
     } else if (gph > kWave) {
       if (lane == 0) *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa;
@@ -700,17 +749,27 @@ int launch(void (*kernel)(Args...), dim3 grid, dim3 block, uint32_t lds_bytes,
              : KVSTORE_ERR_HIP;
 }
 
-// Resident copy waves per CU: enough for about 28 KiB of loads in flight per
-// CU, at least 8 and at most 32 (every wave slot).  The copy writes rows at
-// scattered slots; with every wave slot filled the scattered write streams of
-// the 2 KiB-row prefill copy measured ~5% slower, and with 16-20 KiB in
-// flight (8-10 waves of 2 KiB) the loads stall it by ~12%; 14 waves of 2 KiB
-// measured best.  Rows that move fewer bytes per wave get more waves
-// (1152-byte rows: 25).
-constexpr int64_t kCopyLoadBytesPerCU = 28 * 1024;
+// Resident copy waves per CU, 0 for no cap.  Waves that load 2 KiB or more
+// are capped to about 24 KiB of loads in flight per CU (2 KiB: 12 waves; at
+// least 8): the copy writes rows at scattered slots, and the 2 KiB-row
+// prefill copy measured 48.6 us at 12 resident waves against 49.1 at 10,
+// 49.3 at 14, 49.4 at 16, 55 at 8 and 51.2 uncapped.  Smaller waves run
+// uncapped: the 1152-byte rows of the wide strided copy measured 9.47 us
+// uncapped, 9.49 at 22 waves and 9.9 at 18.
+constexpr int64_t kCopyLoadBytesPerCU = 24 * 1024;
 inline int64_t copy_waves_per_cu(int64_t load_bytes_per_wave) {
-  const int64_t w = (kCopyLoadBytesPerCU + load_bytes_per_wave / 2) / load_bytes_per_wave;
-  return w < 8 ? 8 : w > 32 ? 32 : w;
+  if (load_bytes_per_wave < 2048) return 0;
+  const int64_t w = kCopyLoadBytesPerCU / load_bytes_per_wave;
+  return w < 8 ? 8 : w;
+}
+
+// gfx950 allocates LDS to a block in units of 1280 bytes (a block asking for
+// 23,405 bytes occupies 24,320: six such blocks fit in 160 KiB, not seven),
+// so the size that lets n blocks share a CU is rounded down to that unit.
+constexpr int64_t kLdsGranule = 1280;
+inline uint32_t lds_for_blocks(int64_t lds_per_cu, int64_t blocks) {
+  if (lds_per_cu <= 0 || blocks <= 0) return 0;
+  return (uint32_t)(lds_per_cu / blocks / kLdsGranule * kLdsGranule);
 }
 
 // Tokens of one launch.  A grid with one wave per token then stays at 2^30
@@ -775,11 +834,11 @@ int launch_copy_vw(const CopyParams& p, hipStream_t stream) {
   // The kernel uses no LDS; the dynamic allocation only caps residency (tuned
   // for 16-byte lanes, where a wave has the most bytes in flight).  A wave
   // loads one row slice of K or of V.
-  const int64_t lds = VW == 16 ? lds_per_cu() : 0;
   const int64_t slice_bytes = (int64_t)per_wave * kChunk;
   const int64_t wave_bytes = p.row_bytes < slice_bytes ? (int64_t)p.row_bytes : slice_bytes;
-  const int64_t blocks_per_cu = copy_waves_per_cu(wave_bytes) / kCopyWavesPerBlock;
-  const uint32_t lds_bytes = lds > 0 ? (uint32_t)(lds / blocks_per_cu) : 0;
+  const int64_t waves_per_cu = VW == 16 ? copy_waves_per_cu(wave_bytes) : 0;
+  const uint32_t lds_bytes =
+      waves_per_cu > 0 ? lds_for_blocks(lds_per_cu(), waves_per_cu / kCopyWavesPerBlock) : 0;
   switch (per_wave) {
     case 1: return launch(kvstore_copy_kernel<VW, 1, IdxT>, grid, block, lds_bytes, stream, p);
     case 2: return launch(kvstore_copy_kernel<VW, 2, IdxT>, grid, block, lds_bytes, stream, p);
@@ -822,24 +881,31 @@ int launch_fp8_passes(const Fp8Params& p, bool flat, bool fp16, bool i64, bool e
               : launch_fp8_fmt<kPasses, false>(p, flat, fp16, i64, grid, stream);
 }
 
-template <int kPasses, bool kFlat, bool kFp16>
+template <int kPasses, bool kFlat, bool kFp16, bool kPerHead>
 int launch_dyn_idx(const Fp8DynParams& d, bool i64, dim3 grid, hipStream_t stream) {
   const dim3 block(kBlockThreads);
   if (i64)
-    return launch(kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, int64_t>, grid, block, 0,
-                  stream, d);
-  return launch(kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, int32_t>, grid, block, 0,
-                stream, d);
+    return launch(kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, kPerHead, int64_t>, grid,
+                  block, 0, stream, d);
+  return launch(kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, kPerHead, int32_t>, grid, block,
+                0, stream, d);
+}
+
+template <int kPasses, bool kPerHead>
+int launch_dyn_layout(const Fp8DynParams& d, bool flat, bool fp16, bool i64, dim3 grid,
+                      hipStream_t stream) {
+  if (flat)
+    return fp16 ? launch_dyn_idx<kPasses, true, true, kPerHead>(d, i64, grid, stream)
+                : launch_dyn_idx<kPasses, true, false, kPerHead>(d, i64, grid, stream);
+  return fp16 ? launch_dyn_idx<kPasses, false, true, kPerHead>(d, i64, grid, stream)
+              : launch_dyn_idx<kPasses, false, false, kPerHead>(d, i64, grid, stream);
 }
 
 template <int kPasses>
-int launch_dyn_passes(const Fp8DynParams& d, bool flat, bool fp16, bool i64, dim3 grid,
-                      hipStream_t stream) {
-  if (flat)
-    return fp16 ? launch_dyn_idx<kPasses, true, true>(d, i64, grid, stream)
-                : launch_dyn_idx<kPasses, true, false>(d, i64, grid, stream);
-  return fp16 ? launch_dyn_idx<kPasses, false, true>(d, i64, grid, stream)
-              : launch_dyn_idx<kPasses, false, false>(d, i64, grid, stream);
+int launch_dyn_passes(const Fp8DynParams& d, bool per_head, bool flat, bool fp16, bool i64,
+                      dim3 grid, hipStream_t stream) {
+  return per_head ? launch_dyn_layout<kPasses, true>(d, flat, fp16, i64, grid, stream)
+                  : launch_dyn_layout<kPasses, false>(d, flat, fp16, i64, grid, stream);
 }
 
 // Largest byte offset reached by [0, n) * stride must fit in int64 (stride >= 0).
@@ -1143,33 +1209,37 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
   d.vs_stride_page = vs_stride_page_bytes;
   d.vs_stride_offset = vs_stride_offset_bytes;
   d.vs_stride_head = vs_stride_head_bytes;
-  d.per_head = per_head ? 1 : 0;
   const bool flat = fp8_flat(d.base, head_dim);
   const bool fp16 = src_dtype == KVSTORE_SRC_FP16;
   const bool i64 = idx_dtype == KVSTORE_IDX_I64;
   const int64_t waves_units = ceil_div(d.base.units, kWave);
   return launch_in_runs(d, d.base.token_base, d.base.batch, batch, [&](const Fp8DynParams& run) {
     const dim3 grid((uint32_t)ceil_div(run.base.batch, kWavesPerBlock), 2);
-    if (waves_units <= 1) return launch_dyn_passes<1>(run, flat, fp16, i64, grid, stream);
-    if (waves_units <= 2) return launch_dyn_passes<2>(run, flat, fp16, i64, grid, stream);
-    return launch_dyn_passes<4>(run, flat, fp16, i64, grid, stream);
+    if (waves_units <= 1) return launch_dyn_passes<1>(run, per_head, flat, fp16, i64, grid, stream);
+    if (waves_units <= 2) return launch_dyn_passes<2>(run, per_head, flat, fp16, i64, grid, stream);
+    return launch_dyn_passes<4>(run, per_head, flat, fp16, i64, grid, stream);
   });
 }
 
 int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* bad_count) {
-  if (hipStreamSynchronize(stream) != hipSuccess) return KVSTORE_ERR_HIP;
-  DeviceError h;
-  if (hipMemcpyFromSymbol(&h, HIP_SYMBOL(g_kvstore_error), sizeof h, 0,
-                          hipMemcpyDeviceToHost) != hipSuccess)
+  // The flag is taken by the same one-thread kernel as kvstore_take_error, in
+  // stream order, into a per-device result word pair that one check at a time
+  // uses; then the stream is waited for and the pair read.
+  static std::mutex one_check;
+  std::lock_guard<std::mutex> hold(one_check);
+  int64_t* taken = nullptr;
+  if (hipGetSymbolAddress(reinterpret_cast<void**>(&taken), HIP_SYMBOL(g_kvstore_taken)) !=
+      hipSuccess)
     return KVSTORE_ERR_HIP;
-  const DeviceError cleared = {~0ull, 0ull};
-  if (h.bad_count != 0 &&
-      hipMemcpyToSymbol(HIP_SYMBOL(g_kvstore_error), &cleared, sizeof cleared, 0,
-                        hipMemcpyHostToDevice) != hipSuccess)
+  if (launch(kvstore_take_error_kernel, dim3(1), dim3(1), 0, stream, taken) != KVSTORE_OK)
     return KVSTORE_ERR_HIP;
-  if (first_bad_token) *first_bad_token = h.bad_count ? (int64_t)h.first_bad : -1;
-  if (bad_count) *bad_count = h.bad_count;
-  return h.bad_count ? KVSTORE_ERR_OOB : KVSTORE_OK;
+  int64_t h[2];
+  if (hipMemcpyAsync(h, taken, sizeof h, hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return KVSTORE_ERR_HIP;
+  if (first_bad_token) *first_bad_token = h[0];
+  if (bad_count) *bad_count = (uint64_t)h[1];
+  return h[1] ? KVSTORE_ERR_OOB : KVSTORE_OK;
 }
 
 int kvstore_take_error(int64_t* out_device, hipStream_t stream) {

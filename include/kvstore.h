@@ -49,9 +49,11 @@
  * race, and which one lands is undefined (as on the pages).
  *
  * Concurrency: the error flag is one per device and is shared by every store
- * call on that device; calls may run concurrently on several streams, but a
- * kvstore_check_error overlapping a store on another stream may attribute or
- * clear that store's report.
+ * call on that device; calls may run concurrently on several streams.  Each
+ * rejected token is recorded by one atomic update of the flag and each check
+ * or take clears it by one atomic exchange, so a report made while a check or
+ * take runs on another stream lands, whole, in that one or in the next.  The
+ * count of rejected tokens saturates at 2^32 - 1 between two checks.
  */
 #ifndef KVSTORE_H
 #define KVSTORE_H
@@ -234,11 +236,11 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
  * index, KVSTORE_ERR_OOB when some did, KVSTORE_ERR_HIP on a runtime error.
  * first_bad_token (nullable) receives the smallest rejected token position of
  * any call since the last check, or -1; bad_count (nullable) the number of
- * rejected tokens.  This is the only call that synchronises.  The flag is
- * per device and shared by all streams: a store still running on another
- * stream of the device while this call reads and clears the flag may have its
- * report split between this check and the next, or lost, so check once no
- * store is in flight on other streams.
+ * rejected tokens.  This is the only call that synchronises: it enqueues the
+ * flag's take on `stream` (after the stream's earlier work), then waits for
+ * the stream.  The flag is per device and shared by all streams: reports of
+ * stores still running on other streams are counted by this check or by the
+ * next, never split or lost.  Calls from several host threads are serialised.
  */
 int kvstore_check_error(hipStream_t stream, int64_t* first_bad_token, uint64_t* bad_count);
 

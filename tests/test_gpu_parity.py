@@ -215,7 +215,8 @@ def test_fp8_head_shapes(heads, dim):
 
 def test_fp8_flat_and_paged_tensor_api_agree():
     # The page's wrapper accepts a flat [slots, H, D] cache and a paged
-    # [pages, page_size, H, D] cache, 2-D and 3-D inputs; all four give the same bytes.
+    # [pages, page_size, H, D] cache, 2-D and 3-D inputs; all four give the same
+    # bytes, into float8_e4m3fn caches (2-D inputs) and uint8 caches (3-D).
     c = _fp8_case(tokens=200, pages=8)
     H, D, P = c.num_heads, c.head_dim, c.page_size
     k3 = to_dev(c.k).view(torch.bfloat16).view(-1, H, D)
@@ -232,7 +233,9 @@ def test_fp8_flat_and_paged_tensor_api_agree():
             vcv = vc.view(c.slots, H, D) if flat else vc.view(-1, P, H, D)
             kin = k3.reshape(-1, H * D) if two_d else k3
             vin = v3.reshape(-1, H * D) if two_d else v3
-            kv.store_kv_fp8_paged(kin, vin, kcv.view(torch.float8_e4m3fn), vcv, idx, page_size=P,
+            if two_d:
+                kcv, vcv = kcv.view(torch.float8_e4m3fn), vcv.view(torch.float8_e4m3fn)
+            kv.store_kv_fp8_paged(kin, vin, kcv, vcv, idx, page_size=P,
                                   inv_k_scale=ik, inv_v_scale=iv)
             outs.append((kc.cpu().numpy(), vc.cpu().numpy()))
     okc, ovc, _ = oracle.run_case(c)
@@ -380,6 +383,80 @@ def test_fp8_largest_slot_of_the_paged_cache():
     assert len(set(idx.tolist())) == idx.size
     c.indices = idx
     fp8_parity(c)
+
+
+def _with_slots(c, at):
+    """c with indices[pos] = slot for each (pos, slot) of `at` (kept unique)."""
+    idx = c.indices.copy()
+    for pos, slot in at:
+        idx[pos] = slot
+    assert len(set(idx.tolist())) == idx.size
+    c.indices = idx
+    return c
+
+
+def test_copy_largest_slot_of_the_decode_cache():
+    # 2^20 slots x 2 KiB with int64 indices: the last slot ends exactly at
+    # 2^31 bytes, the first offset a 31-bit signed value cannot hold.
+    c = kvgen.workload(2, tokens=64)
+    assert c.indices.dtype == np.int64 and c.slots * c.row_bytes == 1 << 31
+    copy_parity(_with_slots(c, [(0, c.slots - 1), (63, c.slots - 2), (31, c.slots // 2)]))
+
+
+def test_copy_largest_slot_of_the_wide_strided_cache():
+    # 2^19 slots x 1152 B (int64, rows read at a 1280 B stride)
+    c = kvgen.workload(5, tokens=64)
+    assert c.indices.dtype == np.int64 and c.in_stride_bytes == 1280
+    copy_parity(_with_slots(c, [(0, c.slots - 1), (17, c.slots - 2), (63, 0)]))
+
+
+def test_int64_copy_past_4GiB():
+    # 5 * 2^19 slots x 2 KiB = 5 GiB per cache, int64 indices: slots at,
+    # around and well past the 4 GiB byte offset.
+    slots = 5 << 19
+    c = kvgen.workload(2, tokens=96, slots=slots)
+    four = (1 << 32) // c.row_bytes
+    at = [(0, slots - 1), (1, four), (2, four - 1), (3, four + 1), (95, slots - 2), (50, 0)]
+    copy_parity(_with_slots(c, at))
+
+
+def test_int64_fp8_store_past_4GiB():
+    # 5 * 2^20 slots x 1 KiB (pages of 64) = 5 GiB per cache, int64 indices.
+    slots = 5 << 20
+    c = kvgen.workload(4, tokens=128, slots=slots)
+    c.indices = c.indices.astype(np.int64)
+    c.idx_dtype = kvgen.I64
+    four = (1 << 32) // c.row_elems
+    at = [(0, slots - 1), (1, four), (2, four - 1), (3, four + 64), (127, slots - 64), (64, 5)]
+    fp8_parity(_with_slots(c, at))
+
+
+def test_fp8_tensor_api_refuses_foreign_cache_dtypes_before_launch():
+    """fnuz (another bias and NaN encoding), int8, and K/V caches of two
+    dtypes are refused with TypeError; nothing is written."""
+    f = _fp8_case(tokens=40, pages=2)
+    H, D, P = f.num_heads, f.head_dim, f.page_size
+    k = to_dev(f.k).view(torch.bfloat16).view(-1, H, D)
+    v = to_dev(f.v).view(torch.bfloat16).view(-1, H, D)
+    kc = sentinel_cache(f.slots, f.row_elems)
+    vc = sentinel_cache(f.slots, f.row_elems)
+    idx = to_dev(f.indices)
+    ks = torch.zeros((f.slots,), dtype=torch.float32, device=DEV)
+    vs = torch.zeros_like(ks)
+    pk, pv = kc.view(-1, P, H, D), vc.view(-1, P, H, D)
+    for dt in (torch.float8_e4m3fnuz, torch.float8_e5m2fnuz, torch.int8):
+        with pytest.raises(TypeError):
+            kv.store_kv_fp8_paged(k, v, pk.view(dt), pv.view(dt), idx, page_size=P)
+        with pytest.raises(TypeError):
+            kv.store_kv_fp8_paged_dynamic(k, v, pk.view(dt), pv.view(dt), idx, ks, vs, page_size=P)
+    with pytest.raises(TypeError):
+        kv.store_kv_fp8_paged(k, v, pk.view(torch.float8_e4m3fn), pv, idx, page_size=P)
+    with pytest.raises(TypeError):
+        kv.store_kv_fp8_paged_dynamic(k, v, pk.view(torch.float8_e5m2), pv.view(torch.float8_e5m2),
+                                      idx, ks, vs, page_size=P)
+    torch.cuda.synchronize()
+    assert bool((kc == 0xFF).all()) and bool((vc == 0xFF).all()) and bool((ks == 0).all())
+    assert kv.check_error() == (-1, 0)
 
 
 # ---------------------------------------------------------------------------
