@@ -53,6 +53,9 @@ def parse():
                     help="also launch a plain device copy of this size (counter calibration)")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-next", action="store_true", help="skip the next-row measurements")
+    ap.add_argument("--copy-patterns", action="store_true",
+                    help="only time the prefill copy over four destination patterns (12 launches "
+                         "each: 2 untimed, 10 timed; for counter runs) and print that as the line")
     return ap.parse_args()
 
 
@@ -155,6 +158,16 @@ def main():
         if st:
             raise kv.KVStoreError(st, "kvstore_fp8_paged")
 
+    if args.copy_patterns:
+        out = {"metric": "prefill copy launch time by destination pattern", "unit": "us",
+               "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+               "config": {"workload": "prefill copy (32768 tok, 8x128 bf16, int32, 2^21 slots), "
+                                      "index sets replaced per pattern", "rotation_sets": S},
+               "patterns": bench_patterns(kv, torch, kvgen, c3, k3, v3, kc3, vc3, S, sh,
+                                          windows=1, n=10, warm=2)}
+        print(json.dumps(out), flush=True)
+        return
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -210,6 +223,11 @@ def main():
     fp8_us = fp8_ms_total * 1e3 / K
     value = (b3 + b4) / (ms_per_step * 1e-3) / 1e9
 
+    hot = patterns = None
+    if not args.no_next:
+        hot = bench_hot(torch, copy_call, fp8_call, b3, b4)
+        patterns = bench_patterns(kv, torch, kvgen, c3, k3, v3, kc3, vc3, S, sh)
+
     next_rows = None
     if not args.no_next:
         next_rows = bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh)
@@ -219,7 +237,10 @@ def main():
     traffic = stored_traffic()
     if traffic is not None and "wide_fetch_bytes" in traffic:
         wide["traffic"] = int(traffic["wide_fetch_bytes"] + traffic["wide_write_bytes"])
-    plain = None if args.no_next else bench_plain_kernels(torch, dev, b3, c4, S)
+    plain = bound = None
+    if not args.no_next:
+        plain = bench_plain_kernels(torch, dev, b3, c4, S)
+        bound = bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us)
 
     # Launch-bound decode-size figures last: the idle gaps of their
     # single-call latency loop leave the GPU slow to return to full speed for
@@ -290,6 +311,9 @@ def main():
         "wide_strided_copy": wide,
         "next_rows": next_rows,
         "plain_kernels_same_bytes": plain,
+        "serial_bound": bound,
+        "copy_destination_patterns": patterns,
+        "hot_non_rotated": hot,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -315,6 +339,154 @@ def time_calls(torch, call, S, n=50, reps=3, warm=500):
         torch.cuda.synchronize()
         out.append(e0.elapsed_time(e1) * 1e3 / n)
     return statistics.median(out)
+
+
+def bench_hot(torch, copy_call, fp8_call, b3, b4, n=50):
+    """The step's two kernels on one input/index set, the same every call
+    (not rotated): the 256 MB last-level cache can serve part of the reads
+    and absorb part of the writes, so these are not HBM figures; the
+    headline figures are the rotated ones."""
+    out = {"note": "set 0 every call, not rotated: the last-level cache (256 MB) may serve part "
+                   "of each call; secondary figures, not HBM bandwidth"}
+    for name, call, b in (("prefill_copy", copy_call, b3), ("fp8_paged", fp8_call, b4)):
+        us = time_calls(torch, lambda s, call=call: call(0), 1, n=n, warm=100)
+        out[name] = {"avg_launch_us": round(us, 3), "bytes": b,
+                     "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+    return out
+
+
+def bench_patterns(kv, torch, kvgen, c3, k3, v3, kc3, vc3, S, sh, windows=3, n=50, warm=200):
+    """The prefill copy (same rows, same library call) with its index sets
+    replaced by four destination patterns (kvgen.pattern_index_sets):
+    contiguous slots, 16-slot runs inside a 64 MiB extent, the workload's
+    16-slot runs over the 4 GiB cache, single slots over the cache.  Average
+    launch time per pattern (median of `windows` windows of n calls after
+    `warm` calls, HIP events on the launch stream), rotated over S sets."""
+    import numpy as np
+    R, T = c3.row_bytes, c3.num_tokens
+    dev = k3[0].device
+    out = {}
+    for pat in kvgen.DEST_PATTERNS:
+        idx = [torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+               for a in kvgen.pattern_index_sets(c3, pat, S)]
+
+        def call(s):
+            st = kv.kvstore_copy(k3[s].data_ptr(), v3[s].data_ptr(), kc3.data_ptr(), vc3.data_ptr(),
+                                 idx[s].data_ptr(), kv.IDX_I32, 1, R, c3.in_stride_bytes,
+                                 c3.in_stride_bytes, R, T, c3.slots, sh)
+            if st:
+                raise kv.KVStoreError(st, "kvstore_copy")
+
+        us = time_calls(torch, call, S, n=n, reps=windows, warm=warm)
+        b = c3.algorithmic_bytes()
+        out[pat] = {"avg_launch_us": round(us, 3), "GB/s": round(b / (us * 1e-6) / 1e9, 1)}
+        del idx
+    st, _, _ = kv.kvstore_check_error(sh)
+    assert st == kv.OK
+    return out
+
+
+def _plain_lib():
+    """bench_plain.so (built next to this file by __graft_entry__.build()),
+    with its argument types set; None if it is not built."""
+    import ctypes
+    path = os.path.join(ROOT, "bench_plain.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
+    lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_read.argtypes = [vp, vp, i64, u32, vp]
+    lib.bench_plain_write.argtypes = [vp, i64, u32, vp]
+    return lib
+
+
+def plain_copy_us(torch, dev, nbytes, S, n=50):
+    """Average launch time of the hand-written plain contiguous copy moving
+    nbytes in all (half read, half written), rotated over S buffer pairs;
+    None if bench_plain.so is not built."""
+    lib = _plain_lib()
+    if lib is None:
+        return None
+    half = nbytes // 2 // 16 * 16
+    sh = torch.cuda.current_stream().cuda_stream
+    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(s + 1) for s in range(S)]
+    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
+
+    def copy(s):
+        if lib.bench_plain_copy(src[s].data_ptr(), dst[s].data_ptr(), half, sh) != 0:
+            raise RuntimeError("bench_plain_copy failed")
+
+    us = time_calls(torch, copy, S, n=n)
+    del src, dst
+    torch.cuda.empty_cache()
+    return us
+
+
+def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, n=50):
+    """Same-run attainable bound for the step's two kernels.  HBM serves a
+    kernel's read and write streams one after the other, so a kernel that
+    reads r bytes and writes w bytes takes at least r/R + w/W, with R and W
+    the read-only and write-only rates of plain streaming kernels
+    (bench_plain.hip).  Two forms: R and W measured at the kernel's own byte
+    counts (each plain launch pays its own launch ramp, so this bound is the
+    looser one) and at 1 GiB per launch (near the asymptotic rates)."""
+    lib = _plain_lib()
+    if lib is None:
+        return None
+    sh = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(1024, dtype=torch.uint8, device=dev)
+
+    def read_us(nbytes, S):
+        nbytes = (nbytes + 15) // 16 * 16
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(s + 1) for s in range(S)]
+
+        def call(s):
+            if lib.bench_plain_read(bufs[s].data_ptr(), sink.data_ptr(), nbytes, 0x9E3779B9, sh):
+                raise RuntimeError("bench_plain_read failed")
+
+        us = time_calls(torch, call, S, n=n)
+        del bufs
+        torch.cuda.empty_cache()
+        return us
+
+    def write_us(nbytes, S):
+        nbytes = (nbytes + 15) // 16 * 16
+        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(S)]
+
+        def call(s):
+            if lib.bench_plain_write(bufs[s].data_ptr(), nbytes, s, sh):
+                raise RuntimeError("bench_plain_write failed")
+
+        us = time_calls(torch, call, S, n=n)
+        del bufs
+        torch.cuda.empty_cache()
+        return us
+
+    gib = 1 << 30
+    r_inf = gib / (read_us(gib, 3) * 1e-6) / 1e9
+    w_inf = gib / (write_us(gib, 3) * 1e-6) / 1e9
+    out = {"method": "bound = read-only time of r bytes + write-only time of w bytes (plain "
+                     "non-temporal streaming kernels, one wave per 4 KiB, rotated buffers); "
+                     "at_size: both plain launches at the kernel's own byte counts; "
+                     "asymptotic: rates of 1 GiB launches",
+           "read_GBs_1GiB": round(r_inf, 1), "write_GBs_1GiB": round(w_inf, 1)}
+    T3, T4 = c3.num_tokens, c4.num_tokens
+    rows = (("prefill_copy", copy_us, 2 * T3 * c3.row_bytes + T3 * c3.indices.itemsize,
+             2 * T3 * c3.row_bytes, 8),
+            ("fp8_paged", fp8_us, 2 * T4 * 2 * c4.row_elems + T4 * c4.indices.itemsize + 8,
+             2 * T4 * c4.row_elems, 16))
+    for name, k_us, r, w, S in rows:
+        tr, tw = read_us(r, S), write_us(w, S)
+        b_inf = (r / r_inf + w / w_inf) * 1e-3
+        out[name] = {"read_bytes": r, "write_bytes": w, "kernel_us": round(k_us, 3),
+                     "read_only_us": round(tr, 3), "write_only_us": round(tw, 3),
+                     "bound_us_at_size": round(tr + tw, 3),
+                     "frac_of_bound_at_size": round((tr + tw) / k_us, 4),
+                     "bound_us_asymptotic": round(b_inf, 3),
+                     "frac_of_bound_asymptotic": round(b_inf / k_us, 4)}
+    return out
 
 
 def bench_plain_kernels(torch, dev, copy_bytes, c4, S, n=50):
@@ -357,14 +529,9 @@ def bench_hand_plain(torch, dev, copy_bytes, fp8_elems, S, n=50):
     byte count, and the FP8 store's per-wave shape (2 KiB read, 1 KiB
     written) over its wave count, with no index, scatter or conversion.
     Empty if the library is not built."""
-    import ctypes
-    path = os.path.join(ROOT, "bench_plain.so")
-    if not os.path.exists(path):
+    lib = _plain_lib()
+    if lib is None:
         return {}
-    lib = ctypes.CDLL(path)
-    vp, i64 = ctypes.c_void_p, ctypes.c_int64
-    lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
-    lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
     sh = torch.cuda.current_stream().cuda_stream
     out = {}
     half = copy_bytes // 2 // 16 * 16
@@ -483,11 +650,15 @@ def bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh, n=100):
     st, _, _ = kv.kvstore_check_error(sh)
     assert st == kv.OK
     del kc, vc, ks, vs
+    torch.cuda.empty_cache()
+    plain = plain_copy_us(torch, dev, b, S, n)
     return {"copy_tp_share_256B_rows": {
         "workload": "prefill copy with one 128-dim bf16 head per GPU (32768 tok, 256 B rows, "
                     "int32, 2^21 slots in 16-slot pages)",
         "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
-        "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
+        "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "plain_copy_same_bytes_us": None if plain is None else round(plain, 3),
+        "frac_of_plain_copy": None if plain is None else round(plain / us, 4)}}
 
 
 def bench_decode(kv, torch, dev, kvgen, to_dev, n_workload, label):
@@ -659,11 +830,15 @@ def bench_wide_strided(kv, torch, dev, kvgen, to_dev, S=16, n=50):
     assert st == kv.OK
     b = c5.algorithmic_bytes()
     del kc, vc, k, v
+    torch.cuda.empty_cache()
+    plain = plain_copy_us(torch, dev, b, S, n)
     return {"workload": "wide strided copy (8192 tok, 1x576 fp16, input row stride 640 elements, "
                         "int64, 2^19 slots)",
             "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
-            "rotation_sets": S}
+            "rotation_sets": S,
+            "plain_copy_same_bytes_us": None if plain is None else round(plain, 3),
+            "frac_of_plain_copy": None if plain is None else round(plain / us, 4)}
 
 
 def cpu_baseline(c3, c4, reps):

@@ -12,9 +12,18 @@
 //                            contiguous, non-temporal: the FP8 store's
 //                            per-wave shape (2 KiB of bf16 in, 1 KiB of
 //                            e4m3fn out).
+//   bench_plain_read         reads `bytes` bytes of src, one wave per 4 KiB,
+//                            non-temporal; a wave writes one 16-byte word to
+//                            sink only if its XOR of the data equals `magic`
+//                            (so the loads cannot be dropped, and the
+//                            kernel's traffic is its reads alone).
+//   bench_plain_write        writes `bytes` bytes of dst, one wave per 4 KiB,
+//                            non-temporal; each 16-byte word holds its own
+//                            index XOR `value`.
 //
-// Both return 0 when launched, -1 for bad arguments (nothing launched), -5
-// when the launch failed.  src and dst are device pointers, 16-byte aligned.
+// All return 0 when launched, -1 for bad arguments (nothing launched), -5
+// when the launch failed.  src, dst and sink are device pointers, 16-byte
+// aligned (sink: 64 words of 16 bytes).
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -50,7 +59,42 @@ __global__ __launch_bounds__(128) void plain_read2_write1(const u32x4* __restric
   __builtin_nontemporal_store(a ^ b, d + w * 64 + lane);   // 1 KiB = 64 x 16 B
 }
 
+__global__ __launch_bounds__(256) void plain_read(const u32x4* __restrict__ s,
+                                                  u32x4* __restrict__ sink, uint64_t n16,
+                                                  uint32_t magic) {
+  const uint64_t base =
+      ((uint64_t)blockIdx.x * 4 + threadIdx.x / kWave) * (kWave * kChunks) + threadIdx.x % kWave;
+  u32x4 r[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    r[c] = base + c * kWave < n16 ? __builtin_nontemporal_load(s + base + c * kWave)
+                                  : u32x4{0u, 0u, 0u, 0u};
+  const u32x4 x = r[0] ^ r[1] ^ r[2] ^ r[3];
+  if (x.x == magic && x.y == ~magic) sink[threadIdx.x % kWave] = x;
+}
+
+__global__ __launch_bounds__(256) void plain_write(u32x4* __restrict__ d, uint64_t n16,
+                                                   uint32_t value) {
+  const uint64_t base =
+      ((uint64_t)blockIdx.x * 4 + threadIdx.x / kWave) * (kWave * kChunks) + threadIdx.x % kWave;
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t i = base + c * kWave;
+    if (i < n16) {
+      const uint32_t w = (uint32_t)i ^ value;
+      __builtin_nontemporal_store(u32x4{w, w, w, w}, d + i);
+    }
+  }
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Blocks of four 4 KiB waves covering n16 16-byte words; 0 if too many.
+uint64_t stream_blocks(uint64_t n16) {
+  const uint64_t per_block = 4ull * kWave * kChunks;
+  const uint64_t blocks = (n16 + per_block - 1) / per_block;
+  return blocks > 0x7FFFFFFFull ? 0 : blocks;
+}
 
 }  // namespace
 
@@ -73,5 +117,27 @@ extern "C" int bench_plain_read2_write1(const void* src, void* dst, int64_t wave
   const uint64_t blocks = ((uint64_t)waves + 1) / 2;
   hipLaunchKernelGGL(plain_read2_write1, dim3((uint32_t)blocks), dim3(128), 0, stream,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), (uint64_t)waves);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int bench_plain_read(const void* src, void* sink, int64_t bytes, uint32_t magic,
+                                hipStream_t stream) {
+  if (!src || !sink || bytes <= 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(sink))
+    return -1;
+  const uint64_t n16 = (uint64_t)bytes / 16;
+  const uint64_t blocks = stream_blocks(n16);
+  if (blocks == 0) return -1;
+  hipLaunchKernelGGL(plain_read, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(sink), n16, magic);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int bench_plain_write(void* dst, int64_t bytes, uint32_t value, hipStream_t stream) {
+  if (!dst || bytes <= 0 || bytes % 16 != 0 || !aligned16(dst)) return -1;
+  const uint64_t n16 = (uint64_t)bytes / 16;
+  const uint64_t blocks = stream_blocks(n16);
+  if (blocks == 0) return -1;
+  hipLaunchKernelGGL(plain_write, dim3((uint32_t)blocks), dim3(256), 0, stream,
+                     static_cast<u32x4*>(dst), n16, value);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }

@@ -244,3 +244,42 @@ def all_patterns_case(src_dtype: str, inv_k_bits=None, inv_v_bits=None) -> Case:
                 num_heads=8, head_dim=128, in_stride_elems=1024, k=k, v=v, indices=idx,
                 idx_dtype=I32, slots=128, page_size=64, inv_k_bits=inv_k_bits,
                 inv_v_bits=inv_v_bits, seed=0)
+
+
+DEST_PATTERNS = ("contiguous", "runs16_in_64MiB", "workload", "single_slots")
+
+
+def pattern_index_sets(case: Case, pattern: str, count: int, seed: int = 4242) -> list:
+    """``count`` pairwise-disjoint index arrays for ``case`` that send its
+    tokens to the cache in one of four destination patterns, to take apart
+    what the destination layout costs a store (the rows, token order and
+    index type stay those of the case):
+
+    * ``contiguous``: set s stores to slots [s*T, (s+1)*T);
+    * ``runs16_in_64MiB``: 16-slot runs in random page order, each set inside
+      its own extent of T slots (64 MiB for 2 KiB rows);
+    * ``workload``: the case's own scheme (``disjoint_index_sets``);
+    * ``single_slots``: single slots drawn uniformly over the whole cache.
+    """
+    T, dt = case.num_tokens, case.indices.dtype
+    if pattern == "workload":
+        return disjoint_index_sets(case, count)
+    if count * T > case.slots:
+        raise ValueError("not enough slots for disjoint sets")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if pattern == "contiguous":
+        return [np.arange(s * T, (s + 1) * T, dtype=np.int64).astype(dt) for s in range(count)]
+    if pattern == "runs16_in_64MiB":
+        if T % 16:
+            raise ValueError("token count must be a multiple of 16")
+        pages = T // 16
+        t = np.arange(T, dtype=np.int64)
+        out = []
+        for s in range(count):
+            perm = rng.permutation(pages).astype(np.int64) + s * pages
+            out.append((perm[t // 16] * 16 + t % 16).astype(dt))
+        return out
+    if pattern == "single_slots":
+        pick = rng.permutation(case.slots)[:count * T].astype(np.int64)
+        return [pick[s * T:(s + 1) * T].astype(dt) for s in range(count)]
+    raise ValueError(f"unknown destination pattern {pattern!r}")

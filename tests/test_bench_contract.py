@@ -86,16 +86,26 @@ def test_plain_reference_library_exports():
     if not os.path.exists(path):
         pytest.skip("bench_plain.so not built")
     lib = ctypes.CDLL(path)
-    for name in ("bench_plain_copy", "bench_plain_read2_write1"):
+    for name in ("bench_plain_copy", "bench_plain_read2_write1", "bench_plain_read",
+                 "bench_plain_write"):
         assert hasattr(lib, name), name
-    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
     lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
     lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_read.argtypes = [vp, vp, i64, u32, vp]
+    lib.bench_plain_write.argtypes = [vp, i64, u32, vp]
     # argument errors return before any launch (no GPU needed)
     assert lib.bench_plain_copy(None, None, 16, None) == -1
     assert lib.bench_plain_copy(16, 32, 15, None) == -1
     assert lib.bench_plain_copy(8, 32, 16, None) == -1
     assert lib.bench_plain_read2_write1(16, 32, 0, None) == -1
+    assert lib.bench_plain_read(None, 32, 16, 0, None) == -1
+    assert lib.bench_plain_read(16, None, 16, 0, None) == -1
+    assert lib.bench_plain_read(16, 32, 24, 0, None) == -1
+    assert lib.bench_plain_read(8, 32, 16, 0, None) == -1
+    assert lib.bench_plain_write(None, 16, 0, None) == -1
+    assert lib.bench_plain_write(16, 0, 0, None) == -1
+    assert lib.bench_plain_write(24, 16, 0, None) == -1
 
 
 @pytest.mark.gpu
@@ -116,6 +126,22 @@ def test_plain_reference_kernels_move_the_right_bytes():
         assert lib.bench_plain_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh) == 0
         torch.cuda.synchronize()
         assert torch.equal(dst[:nbytes], src) and int(dst[nbytes:].sum()) == 0
+    lib.bench_plain_read.argtypes = [vp, vp, i64, ctypes.c_uint32, vp]
+    lib.bench_plain_write.argtypes = [vp, i64, ctypes.c_uint32, vp]
+    for nbytes in (16, 4096, 4112, (1 << 20) + 4080):
+        print(f"[gpu-case] plain write / read {nbytes} B", flush=True)
+        dst = torch.zeros(nbytes + 4096, dtype=torch.uint8, device=dev)
+        assert lib.bench_plain_write(dst.data_ptr(), nbytes, 0x5A5A5A5A, sh) == 0
+        torch.cuda.synchronize()
+        words = dst[:nbytes].view(torch.int32).view(-1, 4).cpu()
+        want = (torch.arange(nbytes // 16, dtype=torch.int64) ^ 0x5A5A5A5A).to(torch.int32)
+        assert torch.equal(words, want[:, None].expand(-1, 4))
+        assert int(dst[nbytes:].sum()) == 0
+        # the read-only kernel writes its sink only when a wave's XOR equals magic
+        sink = torch.zeros(1024, dtype=torch.uint8, device=dev)
+        assert lib.bench_plain_read(dst.data_ptr(), sink.data_ptr(), nbytes, 0x9E3779B9, sh) == 0
+        torch.cuda.synchronize()
+        assert int(sink.sum()) == 0
     for waves in (1, 2, 3, 1001):
         print(f"[gpu-case] plain read2/write1 {waves} waves", flush=True)
         src = torch.randint(0, 256, (waves, 2, 1024), dtype=torch.uint8, generator=g).to(dev)
