@@ -561,12 +561,10 @@ __device__ __forceinline__ uint32_t float_to_mag(float f) {
   else return __float_as_uint(f) >> 16;
 }
 
-// max |x| over the 8 elements of one 16-byte vector, as a magnitude pattern.
-// has_nan: some element of the lane may be NaN; then NaN elements are ignored
-// (fmaxf), else the patterns are compared directly, two per packed 16-bit max.
-template <bool kFp16>
-__device__ __forceinline__ uint32_t amax8_mag(u32x4 a, bool has_nan) {
-  if (has_nan) return float_to_mag<kFp16>(amax8<kFp16>(a));
+// max |x| over the 8 elements of one 16-byte vector, as a magnitude pattern:
+// the patterns compared directly, two per packed 16-bit max.  Exact when no
+// element is NaN (a NaN pattern would win; such lanes take amax8 instead).
+__device__ __forceinline__ uint32_t amax8_mag(u32x4 a) {
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   const u16x2 m = __builtin_elementwise_max(
       __builtin_elementwise_max(__builtin_bit_cast(u16x2, a.x & 0x7FFF7FFFu),
@@ -653,12 +651,25 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
   // Every lane takes part in the lane reductions below (groups past the row
   // hold zeros), so the bounds check comes after them.
   bool nan[kPasses];
+  bool some_nan = false;
   uint32_t ma[kPasses], mb[kPasses];
 #pragma unroll
   for (int j = 0; j < kPasses; ++j) {
     nan[j] = any_nan16<kFp16>(a[j], b[j]);
-    ma[j] = amax8_mag<kFp16>(a[j], nan[j]);
-    mb[j] = amax8_mag<kFp16>(b[j], nan[j]);
+    some_nan = some_nan || nan[j];
+    ma[j] = amax8_mag(a[j]);
+    mb[j] = amax8_mag(b[j]);
+  }
+  // Lanes holding a NaN take the maxima that ignore NaN elements, behind a
+  // wave-uniform branch so that the common case does not compute them.
+  if (__builtin_expect(__ballot(some_nan) != 0, 0)) {
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+      if (nan[j]) {
+        ma[j] = float_to_mag<kFp16>(amax8<kFp16>(a[j]));
+        mb[j] = float_to_mag<kFp16>(amax8<kFp16>(b[j]));
+      }
+    }
   }
   if constexpr (!kPerHead) {
     uint32_t mx = 0;
@@ -705,10 +716,13 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
     const float sa = dyn_scale(mag_to_float<kFp16>(ma[j]));
     const float sb = dyn_scale(mag_to_float<kFp16>(mb[j]));
     const float ia = 1.0f / sa, ib = 1.0f / sb;
-    // the inverses are finite and non-zero unless a group holds an infinity
-    const u32x4 q = (!nan[j] && ia != 0.0f && ib != 0.0f)
-                        ? quantize16_no_nan<kFp16, false>(a[j], b[j], ia, ib)
-                        : quantize16<kFp16, false>(a[j], b[j], ia, ib, false);
+    // the inverses are finite and non-zero unless a group holds an infinity;
+    // the exact path sits behind a wave-uniform branch, as above
+    const bool fast = !nan[j] && ia != 0.0f && ib != 0.0f;
+    u32x4 q = quantize16_no_nan<kFp16, false>(a[j], b[j], ia, ib);
+    if (__builtin_expect(__ballot(!fast) != 0, 0)) {
+      if (!fast) q = quantize16<kFp16, false>(a[j], b[j], ia, ib, false);
+    }
     store8_sc1(dst, da[j], u32x2{q.x, q.y});
     if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
     // One lane per group writes its scale: lane 0 of the wave per token; per
