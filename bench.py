@@ -77,7 +77,7 @@ def stored_traffic():
                                            "fp8_fetch_bytes", "fp8_write_bytes")}
     except KeyError:
         return None
-    for k in ("wide_fetch_bytes", "wide_write_bytes"):
+    for k in ("wide_fetch_bytes", "wide_write_bytes", "tp_fetch_bytes", "tp_write_bytes"):
         if k in vals:
             out[k] = float(vals[k])
     return out
@@ -237,6 +237,9 @@ def main():
     traffic = stored_traffic()
     if traffic is not None and "wide_fetch_bytes" in traffic:
         wide["traffic"] = int(traffic["wide_fetch_bytes"] + traffic["wide_write_bytes"])
+    if traffic is not None and "tp_fetch_bytes" in traffic and next_rows is not None:
+        next_rows["copy_tp_share_256B_rows"]["traffic"] = int(traffic["tp_fetch_bytes"] +
+                                                              traffic["tp_write_bytes"])
     plain = bound = None
     if not args.no_next:
         plain = bench_plain_kernels(torch, dev, b3, c4, S)
