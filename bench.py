@@ -389,6 +389,15 @@ def bench_patterns(kv, torch, kvgen, c3, k3, v3, kc3, vc3, S, sh, windows=3, n=5
     return out
 
 
+def _random_bytes(torch, dev, n, seed):
+    """n random bytes on the device: the plain kernels' sources (writing
+    all-zero or constant lines measured faster than varied data on this GPU,
+    so constant fills would flatter the ceilings)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    return torch.randint(0, 256, (n,), dtype=torch.uint8, device=dev, generator=g)
+
+
 def _plain_lib():
     """bench_plain.so (built next to this file by __graft_entry__.build()),
     with its argument types set; None if it is not built."""
@@ -414,7 +423,7 @@ def plain_copy_us(torch, dev, nbytes, S, n=50):
         return None
     half = nbytes // 2 // 16 * 16
     sh = torch.cuda.current_stream().cuda_stream
-    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(s + 1) for s in range(S)]
+    src = [_random_bytes(torch, dev, half, 100 + s) for s in range(S)]
     dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
 
     def copy(s):
@@ -432,9 +441,10 @@ def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, n=50):
     kernel's read and write streams one after the other, so a kernel that
     reads r bytes and writes w bytes takes at least r/R + w/W, with R and W
     the read-only and write-only rates of plain streaming kernels
-    (bench_plain.hip).  Two forms: R and W measured at the kernel's own byte
-    counts (each plain launch pays its own launch ramp, so this bound is the
-    looser one) and at 1 GiB per launch (near the asymptotic rates)."""
+    (bench_plain.hip, each in the fastest form measured).  Two forms: R and W
+    measured at the kernel's own byte counts (each plain launch pays its own
+    launch ramp, so this bound is the looser one) and at 1 GiB per launch
+    (near the asymptotic rates)."""
     lib = _plain_lib()
     if lib is None:
         return None
@@ -443,7 +453,7 @@ def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, n=50):
 
     def read_us(nbytes, S):
         nbytes = (nbytes + 15) // 16 * 16
-        bufs = [torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(s + 1) for s in range(S)]
+        bufs = [_random_bytes(torch, dev, nbytes, 200 + s) for s in range(S)]
 
         def call(s):
             if lib.bench_plain_read(bufs[s].data_ptr(), sink.data_ptr(), nbytes, 0x9E3779B9, sh):
@@ -471,7 +481,8 @@ def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, n=50):
     r_inf = gib / (read_us(gib, 3) * 1e-6) / 1e9
     w_inf = gib / (write_us(gib, 3) * 1e-6) / 1e9
     out = {"method": "bound = read-only time of r bytes + write-only time of w bytes (plain "
-                     "non-temporal streaming kernels, one wave per 4 KiB, rotated buffers); "
+                     "streaming kernels of bench_plain.hip: non-temporal loads, one wave per 2 KiB; "
+                     "sc1 16-byte stores, one wave per 4 KiB; rotated buffers of random bytes); "
                      "at_size: both plain launches at the kernel's own byte counts; "
                      "asymptotic: rates of 1 GiB launches",
            "read_GBs_1GiB": round(r_inf, 1), "write_GBs_1GiB": round(w_inf, 1)}
@@ -501,7 +512,7 @@ def bench_plain_kernels(torch, dev, copy_bytes, c4, S, n=50):
     S buffer sets like the step."""
     out = {}
     half = copy_bytes // 2
-    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(s) for s in range(S)]
+    src = [_random_bytes(torch, dev, half, 400 + s) for s in range(S)]
     dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
     us = time_calls(torch, lambda s: dst[s].copy_(src[s]), S, n=n)
     out["torch_copy"] = {"bytes": 2 * half, "avg_launch_us": round(us, 3),
@@ -538,7 +549,7 @@ def bench_hand_plain(torch, dev, copy_bytes, fp8_elems, S, n=50):
     sh = torch.cuda.current_stream().cuda_stream
     out = {}
     half = copy_bytes // 2 // 16 * 16
-    src = [torch.empty(half, dtype=torch.uint8, device=dev).fill_(s + 1) for s in range(S)]
+    src = [_random_bytes(torch, dev, half, 100 + s) for s in range(S)]
     dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
 
     def copy(s):
@@ -551,7 +562,7 @@ def bench_hand_plain(torch, dev, copy_bytes, fp8_elems, S, n=50):
                               "frac_of_peak": round(2 * half / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
     del src, dst
     waves = fp8_elems // 1024                   # one wave per 1024 elements (2 KiB of bf16)
-    src = [torch.empty(waves * 2048, dtype=torch.uint8, device=dev).fill_(s + 1) for s in range(S)]
+    src = [_random_bytes(torch, dev, waves * 2048, 300 + s) for s in range(S)]
     dst = [torch.empty(waves * 1024, dtype=torch.uint8, device=dev) for _ in range(S)]
 
     def shape(s):

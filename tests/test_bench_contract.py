@@ -6,6 +6,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 import bench
@@ -133,9 +134,12 @@ def test_plain_reference_kernels_move_the_right_bytes():
         dst = torch.zeros(nbytes + 4096, dtype=torch.uint8, device=dev)
         assert lib.bench_plain_write(dst.data_ptr(), nbytes, 0x5A5A5A5A, sh) == 0
         torch.cuda.synchronize()
-        words = dst[:nbytes].view(torch.int32).view(-1, 4).cpu()
-        want = (torch.arange(nbytes // 16, dtype=torch.int64) ^ 0x5A5A5A5A).to(torch.int32)
-        assert torch.equal(words, want[:, None].expand(-1, 4))
+        words = dst[:nbytes].view(torch.int32).view(-1, 4).cpu().numpy().view(np.uint32)
+        i = np.arange(nbytes // 16, dtype=np.uint64)
+        h = ((i * 0x9E3779B1) & 0xFFFFFFFF).astype(np.uint32) ^ np.uint32(0x5A5A5A5A)
+        want = np.stack([h, h ^ np.uint32(0x85EBCA6B), h ^ np.uint32(0xC2B2AE35),
+                         h + np.uint32(0x27D4EB2F)], axis=1)
+        np.testing.assert_array_equal(words, want)
         assert int(dst[nbytes:].sum()) == 0
         # the read-only kernel writes its sink only when a wave's XOR equals magic
         sink = torch.zeros(1024, dtype=torch.uint8, device=dev)
@@ -148,4 +152,8 @@ def test_plain_reference_kernels_move_the_right_bytes():
         dst = torch.zeros(waves + 4, 1024, dtype=torch.uint8, device=dev)
         assert lib.bench_plain_read2_write1(src.data_ptr(), dst.data_ptr(), waves, sh) == 0
         torch.cuda.synchronize()
-        assert torch.equal(dst[:waves], src[:, 0] ^ src[:, 1]) and int(dst[waves:].sum()) == 0
+        # lane l XORs bytes [16l, 16l + 16) of the two halves and stores the
+        # first 8 bytes at 8l, the last 8 at 512 + 8l
+        x = (src[:, 0] ^ src[:, 1]).view(waves, 64, 2, 8)
+        want = torch.cat([x[:, :, 0].reshape(waves, 512), x[:, :, 1].reshape(waves, 512)], dim=1)
+        assert torch.equal(dst[:waves], want) and int(dst[waves:].sum()) == 0
