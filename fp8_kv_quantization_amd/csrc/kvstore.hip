@@ -11,7 +11,8 @@
 //                          token and head (kvstore_fp8_paged_e5m2 / _dynamic).
 //
 // Both are pure data movement, bound by HBM bandwidth: no MFMA, and no LDS
-// traffic (the copy allocates LDS only to cap its residency).
+// traffic for the rows (the copy allocates LDS only to cap its residency; the
+// per-token dynamic store passes one scale per wave through it).
 // Design points for CDNA4:
 //   * one 64-lane wave per (token, K or V, slice of the row); each lane
 //     loads 16 B per access (dwordx4), so one wave access
@@ -99,6 +100,35 @@ __device__ __forceinline__ int64_t load_index(const void* indices, int64_t pos) 
   return (int64_t)static_cast<const IdxT*>(indices)[pos];
 }
 
+// Marks a loaded value as needed at this point.  Placed after the last load
+// of a wave, once per loaded value, it keeps every load of the wave ahead of
+// the first wait for one: left alone, the compiler may sink a load into the
+// (divergent) block of its store, widen an index where it is loaded, or move
+// the wave's scalar index load behind a long computation on the row, and then
+// waits for each load before it issues the next, one memory latency after
+// another.  The value stays in its register; no instruction is emitted.
+template <typename T>
+__device__ __forceinline__ void loaded(T& v) { asm volatile("" : "+v"(v)); }
+
+// The wave's index, loaded after the row loads are issued.  A scalar index
+// load issued before them would be waited for together with the kernel
+// arguments that the row addresses need (scalar loads return out of order,
+// so a wave can only wait for all of them), delaying the row loads by the
+// index latency.  The array address passes through a scalar register at this
+// point, so the load cannot be moved above it; it is read as constant memory
+// (the kernel never writes the index array), which keeps it a scalar load;
+// and the value is asked for right here, before the row data, so that the
+// load is not moved below the waits for the row either.
+template <typename IdxT>
+__device__ __forceinline__ int64_t load_index_after_row_loads(const void* indices, int64_t pos) {
+  uint64_t a = reinterpret_cast<uint64_t>(indices);
+  asm volatile("" : "+s"(a));
+  typedef __attribute__((address_space(4))) const IdxT ConstIdx;
+  int64_t loc = (int64_t)reinterpret_cast<ConstIdx*>(a)[pos];
+  asm volatile("" : "+s"(loc));
+  return loc;
+}
+
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Vector of VW bytes moved by one lane in one access (16, 8 or 4).
@@ -165,18 +195,21 @@ __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const C
   const uint32_t slice = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
 
-  const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
-
   const uint8_t* src =
       is_v ? p.v + (int64_t)token * p.v_stride : p.k + (int64_t)token * p.k_stride;
   const uint32_t col0 = slice * (kChunks * kChunk) + lane * VW;
 
+  // Lanes past the row load the row's last VW bytes and store nothing: no
+  // load sits under a branch.
   T r[kChunks];
 #pragma unroll
   for (int c = 0; c < kChunks; ++c) {
     const uint32_t col = col0 + c * kChunk;
-    if (col < p.row_bytes) r[c] = loadv<VW>(src, col);
+    r[c] = loadv<VW>(src, col < p.row_bytes ? col : p.row_bytes - VW);
   }
+  const int64_t loc = load_index_after_row_loads<IdxT>(p.indices, (int64_t)token * p.idx_stride);
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) loaded(r[c]);
 
   if (loc < 0 || loc >= p.size_limit) {
     if (lane == 0 && slice == 0 && !is_v) report_bad_token(token);
@@ -621,9 +654,13 @@ template <int kPasses, bool kFlat, bool kFp16, bool kPerHead, typename IdxT>
 __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(const Fp8DynParams d) {
   const Fp8Params& p = d.base;
   const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t i = wave_uniform(blockIdx.x * kWavesPerBlock + threadIdx.x / kWave);
-  if (i >= p.batch) return;
-  const uint32_t token = p.token_base + i;
+  const uint32_t w = threadIdx.x / kWave;
+  const uint32_t i = wave_uniform(blockIdx.x * kWavesPerBlock + w);
+  // Per token, the waves of a block meet at a barrier before their stores,
+  // so a wave past the batch works on the last token and stores nothing.
+  const bool valid = i < p.batch;
+  if (kPerHead && !valid) return;
+  const uint32_t token = p.token_base + (valid ? i : p.batch - 1);
   const bool is_v = blockIdx.y != 0;
 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
@@ -650,15 +687,18 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
   }
   // Every lane takes part in the lane reductions below (groups past the row
   // hold zeros), so the bounds check comes after them.
+  // NaN patterns are the largest magnitude patterns, so a pass holds a NaN
+  // exactly when its largest pattern lies above the infinity's.
+  constexpr uint32_t kInfMag = kFp16 ? 0x7C00u : 0x7F80u;
   bool nan[kPasses];
   bool some_nan = false;
   uint32_t ma[kPasses], mb[kPasses];
 #pragma unroll
   for (int j = 0; j < kPasses; ++j) {
-    nan[j] = any_nan16<kFp16>(a[j], b[j]);
-    some_nan = some_nan || nan[j];
     ma[j] = amax8_mag(a[j]);
     mb[j] = amax8_mag(b[j]);
+    nan[j] = max(ma[j], mb[j]) > kInfMag;
+    some_nan = some_nan || nan[j];
   }
   // Lanes holding a NaN take the maxima that ignore NaN elements, behind a
   // wave-uniform branch so that the common case does not compute them.
@@ -689,10 +729,7 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
     }
   }
 
-  if (loc < 0 || loc >= p.size_limit) {
-    if (lane == 0 && !is_v) report_bad_token(token);
-    return;
-  }
+  const bool in_range = loc >= 0 && loc < p.size_limit;
   int64_t page, off;
   if (p.page_shift >= 0) {
     page = loc >> p.page_shift;
@@ -701,21 +738,47 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
     page = loc / p.page_size;
     off = loc - page * p.page_size;
   }
-  const __amdgpu_buffer_rsrc_t dst = row_rsrc(t.cache + page * t.c_page + off * t.c_offset);
   uint8_t* scales = is_v ? d.v_scales + page * d.vs_stride_page + off * d.vs_stride_offset
                          : d.k_scales + page * d.ks_stride_page + off * d.ks_stride_offset;
   const int64_t s_head = is_v ? d.vs_stride_head : d.ks_stride_head;
   // per-head scales need gph to be a power of two (checked on the host): the
   // head of group g is g >> log2(gph)
   const uint32_t gsh = __builtin_ctz(gph);
+  float sa[kPasses], sb[kPasses];
+#pragma unroll
+  for (int j = 0; j < kPasses; ++j) {
+    sa[j] = dyn_scale(mag_to_float<kFp16>(ma[j]));
+    sb[j] = dyn_scale(mag_to_float<kFp16>(mb[j]));
+  }
+
+  if constexpr (!kPerHead) {
+    // The token scales of the block's waves (consecutive tokens) go through
+    // LDS to wave 0, which stores them with one instruction: where the tokens
+    // sit in consecutive slots the scales leave as one memory request instead
+    // of one per wave (18.1 against 18.7 us on the 16384-token FP8 workload;
+    // per-head scales measured no gain).  Every wave reaches the barrier.
+    __shared__ float s_val[kWavesPerBlock];
+    __shared__ float* s_at[kWavesPerBlock];
+    if (lane == 0) {
+      s_val[w] = sa[0];
+      s_at[w] = valid && in_range ? reinterpret_cast<float*>(scales) : nullptr;
+    }
+    __syncthreads();
+    if (w == 0 && lane < (uint32_t)kWavesPerBlock && s_at[lane] != nullptr)
+      *s_at[lane] = s_val[lane];
+  }
+  if (!valid) return;
+  if (!in_range) {
+    if (lane == 0 && !is_v) report_bad_token(token);
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t dst = row_rsrc(t.cache + page * t.c_page + off * t.c_offset);
 #pragma unroll
   for (int j = 0; j < kPasses; ++j) {
     const uint32_t g = j * (2u * kWave) + lane;
     if (g >= groups) continue;
     const bool has_b = g + kWave < groups;
-    const float sa = dyn_scale(mag_to_float<kFp16>(ma[j]));
-    const float sb = dyn_scale(mag_to_float<kFp16>(mb[j]));
-    const float ia = 1.0f / sa, ib = 1.0f / sb;
+    const float ia = 1.0f / sa[j], ib = 1.0f / sb[j];
     // the inverses are finite and non-zero unless a group holds an infinity;
     // the exact path sits behind a wave-uniform branch, as above
     const bool fast = !nan[j] && ia != 0.0f && ib != 0.0f;
@@ -725,19 +788,20 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
     }
     store8_sc1(dst, da[j], u32x2{q.x, q.y});
     if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
-    // One lane per group writes its scale: lane 0 of the wave per token; per
-    // head, the first of each head's gph lanes (for gph = 128, lane 0 of the
-    // pass), for the head of each of its two groups.
-    if constexpr (!kPerHead) {
-      if (g == 0) *reinterpret_cast<float*>(scales) = sa;
-    } else if (gph > kWave) {
-      if (lane == 0) *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa;
-    } else if ((lane & (gph - 1)) == 0) {
-      *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa;
-      if (has_b) *reinterpret_cast<float*>(scales + ((g + kWave) >> gsh) * s_head) = sb;
+    // Per head, one lane per group writes its scale: the first of each
+    // head's gph lanes (for gph = 128, lane 0 of the pass), for the head of
+    // each of its two groups.
+    if constexpr (kPerHead) {
+      if (gph > kWave) {
+        if (lane == 0) *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa[j];
+      } else if ((lane & (gph - 1)) == 0) {
+        *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa[j];
+        if (has_b) *reinterpret_cast<float*>(scales + ((g + kWave) >> gsh) * s_head) = sb[j];
+      }
     }
   }
 }
+
 // ---------------------------------------------------------------------------
 // Host side: validation, dispatch, launch.
 // ---------------------------------------------------------------------------
