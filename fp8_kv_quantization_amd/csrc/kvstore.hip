@@ -49,6 +49,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;                     // lanes per wavefront (CDNA)
 constexpr int kWavesPerBlock = 2;             // fp8 kernels
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
+// fp8 kernel with dynamic scales: per token, the block's waves store their
+// scales with one instruction (4 waves: 17.97 us against 18.08 for 2 and
+// 18.15 for 8 on the 16384-token workload)
+constexpr int kDynWavesPerBlock = 4;
 constexpr int kCopyWavesPerBlock = 2;         // copy kernel
 constexpr int kCopyBlockThreads = kWave * kCopyWavesPerBlock;
 constexpr int kMaxChunksPerWave = 4;          // 4 KiB of K or of V in flight per wave
@@ -641,7 +645,7 @@ __device__ __forceinline__ float dyn_scale(float amax) {
   return __builtin_fmaxf(amax / 448.0f, 1.17549435e-38f);
 }
 
-// Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = 2: K (0) or
+// Grid: x = ceil(batch / kDynWavesPerBlock), one wave per token; y = 2: K (0) or
 // V (1).  The wave holds the tensor's whole row: kPasses passes of 1024
 // elements, as in the static store (lane l takes 8-element groups l and
 // l + 64 of each pass).  kPerHead false: one scale covers the row.  Per head,
@@ -651,11 +655,11 @@ __device__ __forceinline__ float dyn_scale(float amax) {
 // taken on the 15-bit magnitude patterns of the 16-bit inputs and converted
 // to fp32 once per group.
 template <int kPasses, bool kFlat, bool kFp16, bool kPerHead, typename IdxT>
-__global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(const Fp8DynParams d) {
+__global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic_kernel(const Fp8DynParams d) {
   const Fp8Params& p = d.base;
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t w = threadIdx.x / kWave;
-  const uint32_t i = wave_uniform(blockIdx.x * kWavesPerBlock + w);
+  const uint32_t i = wave_uniform(blockIdx.x * kDynWavesPerBlock + w);
   // Per token, the waves of a block meet at a barrier before their stores,
   // so a wave past the batch works on the last token and stores nothing.
   const bool valid = i < p.batch;
@@ -755,16 +759,17 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_dynamic_kernel(cons
     // The token scales of the block's waves (consecutive tokens) go through
     // LDS to wave 0, which stores them with one instruction: where the tokens
     // sit in consecutive slots the scales leave as one memory request instead
-    // of one per wave (18.1 against 18.7 us on the 16384-token FP8 workload;
-    // per-head scales measured no gain).  Every wave reaches the barrier.
-    __shared__ float s_val[kWavesPerBlock];
-    __shared__ float* s_at[kWavesPerBlock];
+    // of one per wave (two waves: 18.1 against 18.7 us on the 16384-token FP8
+    // workload; per-head scales measured no gain).  Every wave reaches the
+    // barrier.
+    __shared__ float s_val[kDynWavesPerBlock];
+    __shared__ float* s_at[kDynWavesPerBlock];
     if (lane == 0) {
       s_val[w] = sa[0];
       s_at[w] = valid && in_range ? reinterpret_cast<float*>(scales) : nullptr;
     }
     __syncthreads();
-    if (w == 0 && lane < (uint32_t)kWavesPerBlock && s_at[lane] != nullptr)
+    if (w == 0 && lane < (uint32_t)kDynWavesPerBlock && s_at[lane] != nullptr)
       *s_at[lane] = s_val[lane];
   }
   if (!valid) return;
@@ -961,7 +966,7 @@ int launch_fp8_passes(const Fp8Params& p, bool flat, bool fp16, bool i64, bool e
 
 template <int kPasses, bool kFlat, bool kFp16, bool kPerHead>
 int launch_dyn_idx(const Fp8DynParams& d, bool i64, dim3 grid, hipStream_t stream) {
-  const dim3 block(kBlockThreads);
+  const dim3 block(kWave * kDynWavesPerBlock);
   if (i64)
     return launch(kvstore_fp8_dynamic_kernel<kPasses, kFlat, kFp16, kPerHead, int64_t>, grid,
                   block, 0, stream, d);
@@ -1292,7 +1297,7 @@ int kvstore_fp8_paged_dynamic(const void* k, const void* v, void* k_cache, void*
   const bool i64 = idx_dtype == KVSTORE_IDX_I64;
   const int64_t waves_units = ceil_div(d.base.units, kWave);
   return launch_in_runs(d, d.base.token_base, d.base.batch, batch, [&](const Fp8DynParams& run) {
-    const dim3 grid((uint32_t)ceil_div(run.base.batch, kWavesPerBlock), 2);
+    const dim3 grid((uint32_t)ceil_div(run.base.batch, kDynWavesPerBlock), 2);
     if (waves_units <= 1) return launch_dyn_passes<1>(run, per_head, flat, fp16, i64, grid, stream);
     if (waves_units <= 2) return launch_dyn_passes<2>(run, per_head, flat, fp16, i64, grid, stream);
     return launch_dyn_passes<4>(run, per_head, flat, fp16, i64, grid, stream);
