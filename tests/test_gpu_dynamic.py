@@ -225,3 +225,41 @@ def test_dynamic_tensor_api_flat_and_paged(per_head):
         np.testing.assert_array_equal(vc.cpu().numpy(), ovc)
         np.testing.assert_array_equal(ks.view(torch.int32).cpu().numpy().view(np.uint32).reshape(oks.shape), oks)
         np.testing.assert_array_equal(vs.view(torch.int32).cpu().numpy().view(np.uint32).reshape(ovs.shape), ovs)
+
+
+@pytest.mark.parametrize("per_head", [False, True])
+@pytest.mark.parametrize("tokens", [1, 2, 3, 5, 6, 7, 9, 13])
+def test_dynamic_partial_blocks_and_bad_tokens(tokens, per_head):
+    """Batches that leave the last block of waves partly empty, with a bad
+    index at a different position of a block in each case: per token, the
+    waves of a block hand their scales to one store, and every other token's
+    row and scale must still land exactly, the bad token's not at all."""
+    c = fp8_case(tokens=tokens, pages=2)
+    limit = 100
+    idx = np.random.Generator(np.random.PCG64(tokens)).permutation(limit)[:tokens].astype(np.int32)
+    bad = {1: 0, 2: 1, 3: 2, 5: 4, 6: 1, 7: 5, 9: 8, 13: 6}[tokens]
+    idx[bad] = limit + bad
+    c.indices = idx
+    kc = sentinel_cache(128, 1024)
+    vc = sentinel_cache(128, 1024)
+    G = 8 if per_head else 1
+    ks = sentinel_cache(128, 4 * G)
+    vs = sentinel_cache(128, 4 * G)
+    _say(f"dynamic partial block per_head={per_head} T={tokens} bad={bad}")
+    assert run_dynamic(c, per_head, kc, vc, ks, vs, size_limit=limit) == kv.OK
+    assert check_flag() == (kv.ERR_OOB, bad, 1)
+    okc = np.full((128, 1024), 0xFF, dtype=np.uint8)
+    ovc = np.full_like(okc, 0xFF)
+    oks = np.full((128, 4 * G), 0xFF, dtype=np.uint8)
+    ovs = np.full_like(oks, 0xFF)
+    st = oracle.fp8_paged_dynamic(c.k, c.v, okc, ovc, idx, oks, ovs, src_dtype="bf16",
+                                  num_heads=8, head_dim=128, k_strides=(2048, 256),
+                                  v_strides=(2048, 256), kc_strides=(64 * 1024, 1024, 128),
+                                  vc_strides=(64 * 1024, 1024, 128),
+                                  ks_strides=(64 * 4 * G, 4 * G, 4 if per_head else 0),
+                                  vs_strides=(64 * 4 * G, 4 * G, 4 if per_head else 0),
+                                  per_head=per_head, size_limit=limit, page_size=64)
+    assert st == (tokens - 1, bad, 1)
+    for got, want, nm in ((kc, okc, "k_cache"), (vc, ovc, "v_cache"), (ks, oks, "k_scales"),
+                          (vs, ovs, "v_scales")):
+        assert_cache_equal(got, want, nm)
