@@ -365,56 +365,11 @@ __device__ __forceinline__ uint32_t pack_fp8(float a, float b, float c, float d)
   return u;
 }
 
-// True if any of the 16 source elements is a NaN.  Per 16-bit half,
-// (h & 0x7FFF) + bias reaches bit 15 exactly when the magnitude bits exceed
-// those of infinity (bf16 0x7F80, fp16 0x7C00); the sum never carries out of
-// its half.
-template <bool kFp16>
-__device__ __forceinline__ bool any_nan16(u32x4 a, u32x4 b) {
-  constexpr uint32_t bias = kFp16 ? 0x03FF03FFu : 0x007F007Fu;
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-  uint32_t acc = 0;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc |= (w[i] & 0x7FFF7FFFu) + bias;
-  return (acc & 0x80008000u) != 0;
-}
-
-// Same result as quantize16 when no product can be NaN (no NaN input, scales
-// finite and non-zero): the clamp is one v_med3_f32 and no NaN fix-up is needed.
-template <bool kFp16, bool kE5M2>
-__device__ __forceinline__ u32x4 quantize16_no_nan(u32x4 a, u32x4 b, float inv_a, float inv_b) {
-  constexpr float M = fp8_max<kE5M2>();
-  u32x4 out;
-  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t w0 = w[2 * i], w1 = w[2 * i + 1];
-    const float inv = i < 2 ? inv_a : inv_b;
-    float e0, e1, e2, e3;
-    if constexpr (kFp16) {
-      e0 = f16_lo(w0); e1 = f16_hi(w0); e2 = f16_lo(w1); e3 = f16_hi(w1);
-    } else {
-      e0 = bf16_lo(w0); e1 = bf16_hi(w0); e2 = bf16_lo(w1); e3 = bf16_hi(w1);
-    }
-    e0 = __builtin_amdgcn_fmed3f(__fmul_rn(e0, inv), -M, M);
-    e1 = __builtin_amdgcn_fmed3f(__fmul_rn(e1, inv), -M, M);
-    e2 = __builtin_amdgcn_fmed3f(__fmul_rn(e2, inv), -M, M);
-    e3 = __builtin_amdgcn_fmed3f(__fmul_rn(e3, inv), -M, M);
-    int q = cvt_pk<kE5M2>(e0, e1, 0, false);
-    q = cvt_pk<kE5M2>(e2, e3, q, true);
-    out[i] = (uint32_t)q;
-  }
-  return out;
-}
-
 // 16 source elements (two 16-byte vectors) -> 16 FP8 bytes: the 8 elements
 // of a scaled by inv_a give bytes 0-7, the 8 of b scaled by inv_b bytes 8-15.
-// scale_ok: both inverse scales are finite and non-zero.
+// The exact path: clamp with NaN passed through, then the NaN code fix-up.
 template <bool kFp16, bool kE5M2>
-__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv_a, float inv_b,
-                                            bool scale_ok) {
-  if (scale_ok && !any_nan16<kFp16>(a, b))
-    return quantize16_no_nan<kFp16, kE5M2>(a, b, inv_a, inv_b);
+__device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv_a, float inv_b) {
   u32x4 out;
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -431,6 +386,55 @@ __device__ __forceinline__ u32x4 quantize16(u32x4 a, u32x4 b, float inv_a, float
                              scale_sat<kE5M2>(e2, inv), scale_sat<kE5M2>(e3, inv));
   }
   return out;
+}
+
+// 16 source elements -> 16 FP8 bytes with no clamp before the conversion.
+// Where no byte comes out as a NaN or infinity code this equals quantize16:
+// a product between the largest finite value and half a step above it
+// rounds down to that value anyway.  A NaN product, or one further out,
+// gives such a code (gfx950 converts them to NaN, e5m2 also to infinity).
+template <bool kFp16, bool kE5M2>
+__device__ __forceinline__ u32x4 quantize16_unclamped(u32x4 a, u32x4 b, float inv_a, float inv_b) {
+  u32x4 out;
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w0 = w[2 * i], w1 = w[2 * i + 1];
+    const float inv = i < 2 ? inv_a : inv_b;
+    float e0, e1, e2, e3;
+    if constexpr (kFp16) {
+      e0 = f16_lo(w0); e1 = f16_hi(w0); e2 = f16_lo(w1); e3 = f16_hi(w1);
+    } else {
+      e0 = bf16_lo(w0); e1 = bf16_hi(w0); e2 = bf16_lo(w1); e3 = bf16_hi(w1);
+    }
+    int q = cvt_pk<kE5M2>(__fmul_rn(e0, inv), __fmul_rn(e1, inv), 0, false);
+    q = cvt_pk<kE5M2>(__fmul_rn(e2, inv), __fmul_rn(e3, inv), q, true);
+    out[i] = (uint32_t)q;
+  }
+  return out;
+}
+
+// True if a byte of q has magnitude bits above the largest finite code
+// (e4m3fn 0x7E, e5m2 0x7B): a NaN or infinity code.
+template <bool kE5M2>
+__device__ __forceinline__ bool any_special(u32x4 q) {
+  constexpr uint32_t bump = kE5M2 ? 0x04040404u : 0x01010101u;
+  const uint32_t acc = ((q.x & 0x7F7F7F7Fu) + bump) | ((q.y & 0x7F7F7F7Fu) + bump) |
+                       ((q.z & 0x7F7F7F7Fu) + bump) | ((q.w & 0x7F7F7F7Fu) + bump);
+  return (acc & 0x80808080u) != 0;
+}
+
+// quantize16 for any inputs and scales: the unclamped conversion, and the
+// exact path for the lanes it leaves with a NaN or infinity code, behind a
+// wave-uniform branch (not taken unless some lane needs it).
+template <bool kFp16, bool kE5M2>
+__device__ __forceinline__ u32x4 quantize16_checked(u32x4 a, u32x4 b, float inv_a, float inv_b) {
+  u32x4 q = quantize16_unclamped<kFp16, kE5M2>(a, b, inv_a, inv_b);
+  const bool special = any_special<kE5M2>(q);
+  if (__builtin_expect(__ballot(special) != 0, 0)) {
+    if (special) q = quantize16<kFp16, kE5M2>(a, b, inv_a, inv_b);
+  }
+  return q;
 }
 
 // Byte offsets of 8-element group g inside one token's source row (16 bytes
@@ -508,9 +512,6 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
   const int64_t loc = load_index<IdxT>(p.indices, (int64_t)token * p.idx_stride);
   const TensorView t = tensor_view(p, is_v, token);
   const float inv = t.inv ? *t.inv : 1.0f;
-  // v_med3 drops NaN, so the single-instruction clamp is used only when no
-  // product can be NaN: finite, non-zero scale and no NaN input.
-  const bool scale_ok = __builtin_fabsf(inv) <= 3.40282347e38f && inv != 0.0f;
 
   // Each pass covers 128 groups of 8 elements (1024 elements): lane l takes
   // groups l and l + 64, so each load instruction of the wave reads 1 KiB of
@@ -545,7 +546,7 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
     const uint32_t g = (slice * kPasses + i) * (2u * kWave) + lane;
     if (g < groups) {
       // bytes 0-7 of q come from group g (a), bytes 8-15 from group g + 64 (b)
-      const u32x4 q = quantize16<kFp16, kE5M2>(a[i], b[i], inv, inv, scale_ok);
+      const u32x4 q = quantize16_checked<kFp16, kE5M2>(a[i], b[i], inv, inv);
       store8_sc1(d, da[i], u32x2{q.x, q.y});
       if (g + kWave < groups) store8_sc1(d, db[i], u32x2{q.z, q.w});
     }
@@ -784,13 +785,7 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
     if (g >= groups) continue;
     const bool has_b = g + kWave < groups;
     const float ia = 1.0f / sa[j], ib = 1.0f / sb[j];
-    // the inverses are finite and non-zero unless a group holds an infinity;
-    // the exact path sits behind a wave-uniform branch, as above
-    const bool fast = !nan[j] && ia != 0.0f && ib != 0.0f;
-    u32x4 q = quantize16_no_nan<kFp16, false>(a[j], b[j], ia, ib);
-    if (__builtin_expect(__ballot(!fast) != 0, 0)) {
-      if (!fast) q = quantize16<kFp16, false>(a[j], b[j], ia, ib, false);
-    }
+    const u32x4 q = quantize16_checked<kFp16, false>(a[j], b[j], ia, ib);
     store8_sc1(dst, da[j], u32x2{q.x, q.y});
     if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
     // Per head, one lane per group writes its scale: the first of each
