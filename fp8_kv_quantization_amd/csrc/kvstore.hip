@@ -124,12 +124,18 @@ __device__ __forceinline__ void loaded(T& v) { asm volatile("" : "+v"(v)); }
 // and the value is asked for right here, before the row data, so that the
 // load is not moved below the waits for the row either.
 template <typename IdxT>
-__device__ __forceinline__ int64_t load_index_after_row_loads(const void* indices, int64_t pos) {
+__device__ __forceinline__ __attribute__((address_space(4))) const IdxT* indices_after_row_loads(
+    const void* indices) {
   uint64_t a = reinterpret_cast<uint64_t>(indices);
   asm volatile("" : "+s"(a));
-  typedef __attribute__((address_space(4))) const IdxT ConstIdx;
-  int64_t loc = (int64_t)reinterpret_cast<ConstIdx*>(a)[pos];
-  asm volatile("" : "+s"(loc));
+  return reinterpret_cast<__attribute__((address_space(4))) const IdxT*>(a);
+}
+__device__ __forceinline__ void index_needed_here(int64_t& loc) { asm volatile("" : "+s"(loc)); }
+
+template <typename IdxT>
+__device__ __forceinline__ int64_t load_index_after_row_loads(const void* indices, int64_t pos) {
+  int64_t loc = (int64_t)indices_after_row_loads<IdxT>(indices)[pos];
+  index_needed_here(loc);
   return loc;
 }
 
@@ -181,59 +187,84 @@ struct CopyParams {
   uint32_t token_base;  // first token of this launch
 };
 
-// One row slice of K or of V per wave.  Grid: x = ceil(batch / kCopyWavesPerBlock)
-// blocks of kCopyWavesPerBlock waves, one wave per token; y = slices of the
-// row, kChunks chunks of 64 * VW bytes each; z = 2: K (0) or V (1).  Blocks
-// are dispatched x first, so a launch moves its K rows, then its V rows; K and
-// V in separate waves of half the bytes let the residency cap be set in
-// finer steps (2 KiB-row copy: 12 waves of 2 KiB per CU, 1.5% faster than
-// the best cap of waves moving 2 KiB of K and 2 KiB of V each).
-template <int VW, int kChunks, typename IdxT>
+// One row slice of K or of V of kTok consecutive tokens per wave.  Grid:
+// x = ceil(batch / (kCopyWavesPerBlock * kTok)) blocks of kCopyWavesPerBlock
+// waves; y = slices of the row, kChunks chunks of 64 * VW bytes each; z = 2:
+// K (0) or V (1).  Blocks are dispatched x first, so a launch moves its K
+// rows, then its V rows; K and V in separate waves of half the bytes let the
+// residency cap be set in finer steps (2 KiB-row copy: 12 waves of 2 KiB per
+// CU, 1.5% faster than the best cap of waves moving 2 KiB of K and 2 KiB of V
+// each).  Several tokens per wave pay off for launches of few waves, where
+// the dispatch of waves and the load-to-store turnaround of each wave weigh
+// more than the bytes.
+template <int VW, int kChunks, int kTok, typename IdxT>
 __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const CopyParams p) {
   typedef typename LaneVec<VW>::type T;
   constexpr uint32_t kChunk = kWave * VW;
   const uint32_t lane = threadIdx.x % kWave;
-  const uint32_t i = wave_uniform(blockIdx.x * kCopyWavesPerBlock + threadIdx.x / kWave);
-  if (i >= p.batch) return;
-  const uint32_t token = p.token_base + i;
+  const uint32_t i0 = wave_uniform((blockIdx.x * kCopyWavesPerBlock + threadIdx.x / kWave) * kTok);
+  if (i0 >= p.batch) return;
   const uint32_t slice = blockIdx.y;
   const bool is_v = blockIdx.z != 0;
-
-  const uint8_t* src =
-      is_v ? p.v + (int64_t)token * p.v_stride : p.k + (int64_t)token * p.k_stride;
+  const uint8_t* base = is_v ? p.v : p.k;
+  const int64_t stride = is_v ? p.v_stride : p.k_stride;
   const uint32_t col0 = slice * (kChunks * kChunk) + lane * VW;
 
-  // Lanes past the row load the row's last VW bytes and store nothing: no
-  // load sits under a branch.
-  T r[kChunks];
+  // Lanes past the row load the row's last VW bytes, tokens past the batch
+  // load the last token, and neither stores: no load sits under a branch.
+  T r[kTok][kChunks];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const uint32_t col = col0 + c * kChunk;
-    r[c] = loadv<VW>(src, col < p.row_bytes ? col : p.row_bytes - VW);
+  for (int t = 0; t < kTok; ++t) {
+    const uint32_t it = i0 + t < p.batch ? i0 + t : p.batch - 1;
+    const uint8_t* src = base + (int64_t)(p.token_base + it) * stride;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const uint32_t col = col0 + c * kChunk;
+      r[t][c] = loadv<VW>(src, col < p.row_bytes ? col : p.row_bytes - VW);
+    }
   }
-  const int64_t loc = load_index_after_row_loads<IdxT>(p.indices, (int64_t)token * p.idx_stride);
+  const auto idx = indices_after_row_loads<IdxT>(p.indices);
+  int64_t loc[kTok];
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) loaded(r[c]);
+  for (int t = 0; t < kTok; ++t) {
+    const uint32_t it = i0 + t < p.batch ? i0 + t : p.batch - 1;
+    loc[t] = (int64_t)idx[(int64_t)(p.token_base + it) * p.idx_stride];
+  }
+#pragma unroll
+  for (int t = 0; t < kTok; ++t) index_needed_here(loc[t]);
+#pragma unroll
+  for (int t = 0; t < kTok; ++t)
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) loaded(r[t][c]);
 
-  if (loc < 0 || loc >= p.size_limit) {
-    if (lane == 0 && slice == 0 && !is_v) report_bad_token(token);
-    return;
-  }
-  uint8_t* dst = (is_v ? p.v_cache : p.k_cache) + loc * p.cache_stride;
+  uint8_t* const cache = is_v ? p.v_cache : p.k_cache;
 #pragma unroll
-  for (int c = 0; c < kChunks; ++c) {
-    const uint32_t col = col0 + c * kChunk;
-    if (col < p.row_bytes) storev<VW>(dst, col, r[c]);
+  for (int t = 0; t < kTok; ++t) {
+    if (i0 + t >= p.batch) break;
+    if (loc[t] < 0 || loc[t] >= p.size_limit) {
+      if (lane == 0 && slice == 0 && !is_v) report_bad_token(p.token_base + i0 + t);
+      continue;
+    }
+    uint8_t* dst = cache + loc[t] * p.cache_stride;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const uint32_t col = col0 + c * kChunk;
+      if (col < p.row_bytes) storev<VW>(dst, col, r[t][c]);
+    }
   }
 }
 
 // Several rows per wave, for rows that need at most 32 lanes.  Each aligned
 // group of 2^group_shift lanes owns kPackRows tokens (indices are per-lane
 // loads); lane c of a group moves bytes [c * VW, c * VW + VW) of each row.
-// All loads of a wave are issued before its stores.  Blocks of
-// kPackWavesPerBlock waves; grid x = ceil(batch / tokens per block).
+// Every lane loads (past the batch the last token, past the row the row's
+// last VW bytes) and only lanes inside both store, so all loads of a wave are
+// issued before its first wait.  Blocks of kPackWavesPerBlock waves; grid
+// x = ceil(batch / tokens per block).  256 B rows of the 32768-token
+// tensor-parallel share: 4 tokens per group (16 per wave) 6.72 us, 2 tokens
+// 8.1, 8 tokens 7.0, 16 tokens 7.3-8.0.
 constexpr int kPackWavesPerBlock = 4;
-constexpr int kPackRows = 2;
+constexpr int kPackRows = 4;
 
 template <int VW, typename IdxT>
 __global__ __launch_bounds__(kWave * kPackWavesPerBlock) void kvstore_copy_packed_kernel(
@@ -244,31 +275,35 @@ __global__ __launch_bounds__(kWave * kPackWavesPerBlock) void kvstore_copy_packe
   const uint32_t rows_per_wave = kWave >> group_shift;
   const uint32_t col = (lane & ((1u << group_shift) - 1)) * VW;
   const bool active = col < p.row_bytes;
+  const uint32_t lcol = active ? col : p.row_bytes - VW;
   T kr[kPackRows], vr[kPackRows];
-  int64_t loc[kPackRows];
+  IdxT idx[kPackRows];
 #pragma unroll
   for (int r = 0; r < kPackRows; ++r) {
     const uint64_t i = ((uint64_t)wave * kPackRows + r) * rows_per_wave + (lane >> group_shift);
-    if (i < p.batch) {
-      const int64_t t = (int64_t)p.token_base + (int64_t)i;
-      loc[r] = load_index<IdxT>(p.indices, t * p.idx_stride);
-      if (active) {
-        kr[r] = loadv<VW>(p.k + t * p.k_stride, col);
-        vr[r] = loadv<VW>(p.v + t * p.v_stride, col);
-      }
-    }
+    const int64_t t = (int64_t)p.token_base + (int64_t)(i < p.batch ? i : p.batch - 1);
+    idx[r] = static_cast<const IdxT*>(p.indices)[t * p.idx_stride];
+    kr[r] = loadv<VW>(p.k + t * p.k_stride, lcol);
+    vr[r] = loadv<VW>(p.v + t * p.v_stride, lcol);
+  }
+#pragma unroll
+  for (int r = 0; r < kPackRows; ++r) {
+    loaded(idx[r]);
+    loaded(kr[r]);
+    loaded(vr[r]);
   }
 #pragma unroll
   for (int r = 0; r < kPackRows; ++r) {
     const uint64_t i = ((uint64_t)wave * kPackRows + r) * rows_per_wave + (lane >> group_shift);
     if (i >= p.batch) continue;
-    if (loc[r] < 0 || loc[r] >= p.size_limit) {
+    const int64_t loc = (int64_t)idx[r];
+    if (loc < 0 || loc >= p.size_limit) {
       if (col == 0) report_bad_token(p.token_base + (uint32_t)i);
       continue;
     }
     if (active) {
-      storev<VW>(p.k_cache + loc[r] * p.cache_stride, col, kr[r]);
-      storev<VW>(p.v_cache + loc[r] * p.cache_stride, col, vr[r]);
+      storev<VW>(p.k_cache + loc * p.cache_stride, col, kr[r]);
+      storev<VW>(p.v_cache + loc * p.cache_stride, col, vr[r]);
     }
   }
 }
@@ -841,6 +876,20 @@ inline int64_t copy_waves_per_cu(int64_t load_bytes_per_wave) {
   return w < 8 ? 8 : w;
 }
 
+// Tokens per copy wave, for rows of up to two chunks, from the row bytes a
+// launch reads: a launch of up to 48 MiB moves 8 tokens per wave (uncapped),
+// a larger one 1 (under the residency cap).  Measured with rows in 16-slot
+// runs over random pages: 8192 tokens of 1 KiB 6.70 against 8.61 us, 2048
+// tokens of 2 KiB 4.25 against 5.22, 12288 tokens of 2 KiB 18.8 against 19.5,
+// the 8192-token wide strided copy 7.86 against 9.51; 16384 tokens of 2 KiB
+// 26.0 against 25.6 and the 32768-token prefill copy 53.0 against 48.6 (2 and
+// 4 tokens fell in between; 16 spilled registers and ran 2-3x slower).
+constexpr int64_t kCopySmallLaunchBytes = 48ll << 20;
+constexpr int kCopySmallLaunchTokens = 8;
+inline int copy_tokens_per_wave(int64_t read_bytes) {
+  return read_bytes <= kCopySmallLaunchBytes ? kCopySmallLaunchTokens : 1;
+}
+
 // gfx950 allocates LDS to a block in units of 1280 bytes (a block asking for
 // 23,405 bytes occupies 24,320: six such blocks fit in 160 KiB, not seven),
 // so the size that lets n blocks share a CU is rounded down to that unit.
@@ -908,20 +957,23 @@ int launch_copy_vw(const CopyParams& p, hipStream_t stream) {
   const int per_wave = (int)(chunks < kMaxChunksPerWave ? chunks : kMaxChunksPerWave);
   const int64_t slices = ceil_div(chunks, per_wave);
   if (slices > kMaxGridY) return KVSTORE_ERR_SHAPE;
-  const dim3 grid((uint32_t)ceil_div(p.batch, kCopyWavesPerBlock), (uint32_t)slices, 2);
+  const int tok = per_wave <= 2 ? copy_tokens_per_wave(2 * (int64_t)p.batch * p.row_bytes) : 1;
+  const dim3 grid((uint32_t)ceil_div(p.batch, (int64_t)kCopyWavesPerBlock * tok), (uint32_t)slices, 2);
   // The kernel uses no LDS; the dynamic allocation only caps residency (tuned
-  // for 16-byte lanes, where a wave has the most bytes in flight).  A wave
-  // loads one row slice of K or of V.
+  // for 16-byte lanes, where a wave has the most bytes in flight).
   const int64_t slice_bytes = (int64_t)per_wave * kChunk;
   const int64_t wave_bytes = p.row_bytes < slice_bytes ? (int64_t)p.row_bytes : slice_bytes;
-  const int64_t waves_per_cu = VW == 16 ? copy_waves_per_cu(wave_bytes) : 0;
+  const int64_t waves_per_cu = VW == 16 && tok == 1 ? copy_waves_per_cu(wave_bytes) : 0;
   const uint32_t lds_bytes =
       waves_per_cu > 0 ? lds_for_blocks(lds_per_cu(), waves_per_cu / kCopyWavesPerBlock) : 0;
-  switch (per_wave) {
-    case 1: return launch(kvstore_copy_kernel<VW, 1, IdxT>, grid, block, lds_bytes, stream, p);
-    case 2: return launch(kvstore_copy_kernel<VW, 2, IdxT>, grid, block, lds_bytes, stream, p);
-    case 3: return launch(kvstore_copy_kernel<VW, 3, IdxT>, grid, block, lds_bytes, stream, p);
-    default: return launch(kvstore_copy_kernel<VW, 4, IdxT>, grid, block, lds_bytes, stream, p);
+  constexpr int M = kCopySmallLaunchTokens;
+  switch (per_wave * 16 + tok) {
+    case 1 * 16 + 1: return launch(kvstore_copy_kernel<VW, 1, 1, IdxT>, grid, block, lds_bytes, stream, p);
+    case 1 * 16 + M: return launch(kvstore_copy_kernel<VW, 1, M, IdxT>, grid, block, lds_bytes, stream, p);
+    case 2 * 16 + 1: return launch(kvstore_copy_kernel<VW, 2, 1, IdxT>, grid, block, lds_bytes, stream, p);
+    case 2 * 16 + M: return launch(kvstore_copy_kernel<VW, 2, M, IdxT>, grid, block, lds_bytes, stream, p);
+    case 3 * 16 + 1: return launch(kvstore_copy_kernel<VW, 3, 1, IdxT>, grid, block, lds_bytes, stream, p);
+    default: return launch(kvstore_copy_kernel<VW, 4, 1, IdxT>, grid, block, lds_bytes, stream, p);
   }
 }
 

@@ -26,7 +26,7 @@ sys.path.insert(0, os.path.join(ROOT, "fp8_kv_quantization_amd"))
 import _build  # noqa: E402
 
 COVERED = (
-    r"kvstore_copy_kernelILi\d+ELi\d+E[il]E",
+    r"kvstore_copy_kernelILi\d+ELi\d+ELi\d+E[il]E",
     r"kvstore_fp8_paged_kernelILi1ELb[01]ELb[01]ELb[01]E[il]E",
     r"kvstore_fp8_dynamic_kernelILi1ELb[01]ELb[01]ELb[01]E[il]E",
 )
@@ -74,8 +74,9 @@ def loads_before_first_wait(body):
 def test_every_row_load_is_in_flight_before_the_first_wait(asm):
     ks = kernels(asm)
     covered = {k: b for k, b in ks.items() if any(re.search(p, k) for p in COVERED)}
-    # 3 lane widths x 4 chunk counts x 2 index types; 16 + 16 FP8 forms
-    assert len(covered) == 24 + 16 + 16, sorted(covered)
+    # 3 lane widths x (4 chunk counts + 2 with several tokens per wave) x 2
+    # index types; 16 + 16 FP8 forms
+    assert len(covered) == 36 + 16 + 16, sorted(covered)
     bad = {}
     for name, body in covered.items():
         before, total = loads_before_first_wait(body)
@@ -86,8 +87,8 @@ def test_every_row_load_is_in_flight_before_the_first_wait(asm):
 
 
 def test_the_index_load_is_issued_with_the_row_loads(asm):
-    """The scalar index load of the copy comes after its row loads (so the
-    row loads do not wait for it) and before its first wait (so the two
+    """The scalar index loads of the copy come after its row loads (so the
+    row loads do not wait for them) and before its first wait (so the
     latencies overlap)."""
     ks = kernels(asm)
     for name, body in ks.items():

@@ -569,6 +569,37 @@ def test_copy_narrow_and_packed_rows(row, stride, ptr_off, idx64):
     assert_cache_equal(vc, ovc, "v_cache")
 
 
+@pytest.mark.parametrize("row,tokens", [(1040, 25000), (1000, 26000), (500, 52000), (2048, 12800),
+                                        (2048, 12000)])
+def test_copy_one_and_eight_token_waves_around_the_launch_size_split(row, tokens):
+    """Copies that read more than 48 MiB of rows move one token per wave,
+    smaller ones eight: each lane width (16, 8, 4 bytes) on the one-token
+    side, and 2 KiB rows just past the split, with bad tokens, every byte
+    against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(row * 7 + tokens))
+    slots = 1 << 16 if row * (1 << 16) < (1 << 27) else 1 << 15
+    slots = max(slots, tokens + 1024)
+    kb = rng.integers(0, 256, (tokens, row), dtype=np.uint8)
+    vb = rng.integers(0, 256, (tokens, row), dtype=np.uint8)
+    idx = rng.permutation(slots)[:tokens].astype(np.int32)
+    idx[7], idx[tokens - 2] = -5, slots
+    c = kvgen.Case(name=f"split{row}", kind="copy", src_dtype="bf16", num_tokens=tokens,
+                   num_heads=1, head_dim=row // 2, in_stride_elems=row // 2,
+                   k=kb.view(np.uint16), v=vb.view(np.uint16), indices=idx, idx_dtype="i32",
+                   slots=slots)
+    _say(f"copy split row={row} tokens={tokens} read={2 * row * tokens / 2**20:.1f} MiB")
+    kc = sentinel_cache(slots, row)
+    vc = sentinel_cache(slots, row)
+    assert run_copy(c, kc, vc) == kv.OK
+    assert check_flag() == (kv.ERR_OOB, 7, 2)
+    okc = np.full((slots, row), 0xFF, dtype=np.uint8)
+    ovc = np.full_like(okc, 0xFF)
+    assert oracle.copy(kb, vb, okc, ovc, idx, row_bytes=row, k_stride=row, v_stride=row,
+                       cache_stride=row, size_limit=slots) == (tokens - 2, 7, 2)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
 def test_copy_packed_rows_out_of_range():
     # 256-byte rows pack four tokens to a wave; bad tokens in one wave must not
     # disturb their neighbours.
