@@ -408,32 +408,42 @@ def _plain_lib():
     lib = ctypes.CDLL(path)
     vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
     lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_copy_chunks.argtypes = [vp, vp, i64, ctypes.c_int, vp]
     lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
     lib.bench_plain_read.argtypes = [vp, vp, i64, u32, vp]
     lib.bench_plain_write.argtypes = [vp, i64, u32, vp]
     return lib
 
 
+PLAIN_COPY_KIB_PER_WAVE = (2, 4, 8)
+
+
 def plain_copy_us(torch, dev, nbytes, S, n=50):
-    """Average launch time of the hand-written plain contiguous copy moving
-    nbytes in all (half read, half written), rotated over S buffer pairs;
-    None if bench_plain.so is not built."""
+    """Average launch time of the fastest hand-written plain contiguous copy
+    moving nbytes in all (half read, half written), rotated over S buffer
+    pairs: the copy with 2, 4 and 8 KiB per wave is timed and the fastest
+    kept (small copies run faster with more bytes per wave).  Returns
+    (us, KiB per wave), or (None, None) if bench_plain.so is not built."""
     lib = _plain_lib()
     if lib is None:
-        return None
+        return None, None
     half = nbytes // 2 // 16 * 16
     sh = torch.cuda.current_stream().cuda_stream
     src = [_random_bytes(torch, dev, half, 100 + s) for s in range(S)]
     dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
+    best = (None, None)
+    for kib in PLAIN_COPY_KIB_PER_WAVE:
+        def copy(s, kib=kib):
+            if lib.bench_plain_copy_chunks(src[s].data_ptr(), dst[s].data_ptr(), half, kib,
+                                           sh) != 0:
+                raise RuntimeError("bench_plain_copy_chunks failed")
 
-    def copy(s):
-        if lib.bench_plain_copy(src[s].data_ptr(), dst[s].data_ptr(), half, sh) != 0:
-            raise RuntimeError("bench_plain_copy failed")
-
-    us = time_calls(torch, copy, S, n=n)
+        us = time_calls(torch, copy, S, n=n)
+        if best[0] is None or us < best[0]:
+            best = (us, kib)
     del src, dst
     torch.cuda.empty_cache()
-    return us
+    return best
 
 
 def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, n=50):
@@ -549,18 +559,11 @@ def bench_hand_plain(torch, dev, copy_bytes, fp8_elems, S, n=50):
     sh = torch.cuda.current_stream().cuda_stream
     out = {}
     half = copy_bytes // 2 // 16 * 16
-    src = [_random_bytes(torch, dev, half, 100 + s) for s in range(S)]
-    dst = [torch.empty(half, dtype=torch.uint8, device=dev) for _ in range(S)]
-
-    def copy(s):
-        if lib.bench_plain_copy(src[s].data_ptr(), dst[s].data_ptr(), half, sh) != 0:
-            raise RuntimeError("bench_plain_copy failed")
-
-    us = time_calls(torch, copy, S, n=n)
+    us, kib = plain_copy_us(torch, dev, 2 * half, S, n)
     out["hand_plain_copy"] = {"bytes": 2 * half, "avg_launch_us": round(us, 3),
+                              "kib_per_wave": kib,
                               "GB/s": round(2 * half / (us * 1e-6) / 1e9, 1),
                               "frac_of_peak": round(2 * half / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
-    del src, dst
     waves = fp8_elems // 1024                   # one wave per 1024 elements (2 KiB of bf16)
     src = [_random_bytes(torch, dev, waves * 2048, 300 + s) for s in range(S)]
     dst = [torch.empty(waves * 1024, dtype=torch.uint8, device=dev) for _ in range(S)]
@@ -665,13 +668,14 @@ def bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh, n=100):
     assert st == kv.OK
     del kc, vc, ks, vs
     torch.cuda.empty_cache()
-    plain = plain_copy_us(torch, dev, b, S, n)
+    plain, plain_kib = plain_copy_us(torch, dev, b, S, n)
     return {"copy_tp_share_256B_rows": {
         "workload": "prefill copy with one 128-dim bf16 head per GPU (32768 tok, 256 B rows, "
                     "int32, 2^21 slots in 16-slot pages)",
         "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
         "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "plain_copy_same_bytes_us": None if plain is None else round(plain, 3),
+        "plain_copy_kib_per_wave": plain_kib,
         "frac_of_plain_copy": None if plain is None else round(plain / us, 4)}}
 
 
@@ -845,13 +849,14 @@ def bench_wide_strided(kv, torch, dev, kvgen, to_dev, S=16, n=50):
     b = c5.algorithmic_bytes()
     del kc, vc, k, v
     torch.cuda.empty_cache()
-    plain = plain_copy_us(torch, dev, b, S, n)
+    plain, plain_kib = plain_copy_us(torch, dev, b, S, n)
     return {"workload": "wide strided copy (8192 tok, 1x576 fp16, input row stride 640 elements, "
                         "int64, 2^19 slots)",
             "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
             "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
             "rotation_sets": S,
             "plain_copy_same_bytes_us": None if plain is None else round(plain, 3),
+            "plain_copy_kib_per_wave": plain_kib,
             "frac_of_plain_copy": None if plain is None else round(plain / us, 4)}
 
 

@@ -8,6 +8,11 @@
 //                            wave per 2 KiB (two 1 KiB wave accesses),
 //                            blocks of 2 waves, non-temporal 16-byte loads
 //                            and stores, full occupancy.
+//   bench_plain_copy_chunks  the same copy with `chunks` (2, 4 or 8) 1 KiB
+//                            wave accesses per wave: small copies run
+//                            faster with more bytes per wave (fewer waves
+//                            to dispatch), large ones with 2; all of a
+//                            wave's loads are issued before its first wait.
 //   bench_plain_read2_write1 `waves` waves, each reading 2 KiB of src and
 //                            writing 1 KiB to dst (the two halves XORed),
 //                            contiguous: the FP8 store's per-wave shape
@@ -107,6 +112,27 @@ __global__ __launch_bounds__(256) void plain_write(uint8_t* __restrict__ d, uint
   }
 }
 
+// kChunks 1 KiB wave accesses per wave; lanes past the end load the last
+// 16-byte word (and store nothing), so no load sits under a branch, and an
+// empty asm operand per loaded value keeps every load ahead of the first wait.
+template <int kChunks>
+__global__ __launch_bounds__(128) void plain_copy_n(const u32x4* __restrict__ s,
+                                                    u32x4* __restrict__ d, uint64_t n16) {
+  const uint64_t base = ((uint64_t)blockIdx.x * 2 + threadIdx.x / kWave) * (kChunks * kWave) +
+                        threadIdx.x % kWave;
+  u32x4 r[kChunks];
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) {
+    const uint64_t i = base + c * kWave;
+    r[c] = __builtin_nontemporal_load(s + (i < n16 ? i : n16 - 1));
+  }
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c) asm volatile("" : "+v"(r[c]));
+#pragma unroll
+  for (int c = 0; c < kChunks; ++c)
+    if (base + c * kWave < n16) __builtin_nontemporal_store(r[c], d + base + c * kWave);
+}
+
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 // Blocks of `per_block` 16-byte words covering n16; 0 if too many.
@@ -125,6 +151,25 @@ extern "C" int bench_plain_copy(const void* src, void* dst, int64_t bytes, hipSt
   if (blocks == 0) return -1;
   hipLaunchKernelGGL(plain_copy, dim3((uint32_t)blocks), dim3(128), 0, stream,
                      static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16);
+  return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int bench_plain_copy_chunks(const void* src, void* dst, int64_t bytes, int chunks,
+                                       hipStream_t stream) {
+  if (!src || !dst || bytes <= 0 || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst) ||
+      (chunks != 2 && chunks != 4 && chunks != 8))
+    return -1;
+  const uint64_t n16 = (uint64_t)bytes / 16;
+  const uint64_t blocks = blocks_for(n16, 2ull * chunks * kWave);
+  if (blocks == 0) return -1;
+  const u32x4* s = static_cast<const u32x4*>(src);
+  u32x4* d = static_cast<u32x4*>(dst);
+  if (chunks == 2)
+    hipLaunchKernelGGL(plain_copy_n<2>, dim3((uint32_t)blocks), dim3(128), 0, stream, s, d, n16);
+  else if (chunks == 4)
+    hipLaunchKernelGGL(plain_copy_n<4>, dim3((uint32_t)blocks), dim3(128), 0, stream, s, d, n16);
+  else
+    hipLaunchKernelGGL(plain_copy_n<8>, dim3((uint32_t)blocks), dim3(128), 0, stream, s, d, n16);
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 

@@ -877,17 +877,23 @@ inline int64_t copy_waves_per_cu(int64_t load_bytes_per_wave) {
 }
 
 // Tokens per copy wave, for rows of up to two chunks, from the row bytes a
-// launch reads: a launch of up to 48 MiB moves 8 tokens per wave (uncapped),
-// a larger one 1 (under the residency cap).  Measured with rows in 16-slot
-// runs over random pages: 8192 tokens of 1 KiB 6.70 against 8.61 us, 2048
-// tokens of 2 KiB 4.25 against 5.22, 12288 tokens of 2 KiB 18.8 against 19.5,
-// the 8192-token wide strided copy 7.86 against 9.51; 16384 tokens of 2 KiB
-// 26.0 against 25.6 and the 32768-token prefill copy 53.0 against 48.6 (2 and
-// 4 tokens fell in between; 16 spilled registers and ran 2-3x slower).
+// launch reads: between 6 and 48 MiB a wave moves 8 tokens (uncapped);
+// otherwise 1 (over 48 MiB under the residency cap).  Measured with rows in
+// 16-slot runs over random pages: 8192 tokens of 1 KiB 6.70 against 8.61
+// us, 2048 tokens of 2 KiB 4.25 against 5.22, 12288 tokens of 2 KiB 18.8
+// against 19.5, the 8192-token wide strided copy 7.86 against 9.51; 16384
+// tokens of 2 KiB 26.0 against 25.6 and the 32768-token prefill copy 53.0
+// against 48.6 (2 and 4 tokens fell in between; 16 spilled registers and
+// ran 2-3x slower).  Below, too few waves are left to fill the chip: 2 KiB
+// rows replayed from a graph, 256 tokens 3.37 against 2.30 us, 1024 tokens
+// 3.86 against 3.37, 2048 tokens 4.23 against 5.19.
+constexpr int64_t kCopySmallLaunchMinBytes = 6ll << 20;
 constexpr int64_t kCopySmallLaunchBytes = 48ll << 20;
 constexpr int kCopySmallLaunchTokens = 8;
 inline int copy_tokens_per_wave(int64_t read_bytes) {
-  return read_bytes <= kCopySmallLaunchBytes ? kCopySmallLaunchTokens : 1;
+  return read_bytes > kCopySmallLaunchMinBytes && read_bytes <= kCopySmallLaunchBytes
+             ? kCopySmallLaunchTokens
+             : 1;
 }
 
 // gfx950 allocates LDS to a block in units of 1280 bytes (a block asking for

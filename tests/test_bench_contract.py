@@ -87,15 +87,21 @@ def test_plain_reference_library_exports():
     if not os.path.exists(path):
         pytest.skip("bench_plain.so not built")
     lib = ctypes.CDLL(path)
-    for name in ("bench_plain_copy", "bench_plain_read2_write1", "bench_plain_read",
-                 "bench_plain_write"):
+    for name in ("bench_plain_copy", "bench_plain_copy_chunks", "bench_plain_read2_write1",
+                 "bench_plain_read", "bench_plain_write"):
         assert hasattr(lib, name), name
     vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
     lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_copy_chunks.argtypes = [vp, vp, i64, ctypes.c_int, vp]
     lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
     lib.bench_plain_read.argtypes = [vp, vp, i64, u32, vp]
     lib.bench_plain_write.argtypes = [vp, i64, u32, vp]
     # argument errors return before any launch (no GPU needed)
+    for chunks in (0, 1, 3, 16):
+        assert lib.bench_plain_copy_chunks(16, 32, 16, chunks, None) == -1
+    assert lib.bench_plain_copy_chunks(None, 32, 16, 2, None) == -1
+    assert lib.bench_plain_copy_chunks(16, 32, 24, 8, None) == -1
+    assert lib.bench_plain_copy_chunks(8, 32, 16, 4, None) == -1
     assert lib.bench_plain_copy(None, None, 16, None) == -1
     assert lib.bench_plain_copy(16, 32, 15, None) == -1
     assert lib.bench_plain_copy(8, 32, 16, None) == -1
@@ -116,6 +122,7 @@ def test_plain_reference_kernels_move_the_right_bytes():
     lib = ctypes.CDLL(os.path.join(ROOT, "bench_plain.so"))
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
     lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
+    lib.bench_plain_copy_chunks.argtypes = [vp, vp, i64, ctypes.c_int, vp]
     lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
     dev = torch.device("cuda:0")
     sh = torch.cuda.current_stream().cuda_stream
@@ -127,6 +134,13 @@ def test_plain_reference_kernels_move_the_right_bytes():
         assert lib.bench_plain_copy(src.data_ptr(), dst.data_ptr(), nbytes, sh) == 0
         torch.cuda.synchronize()
         assert torch.equal(dst[:nbytes], src) and int(dst[nbytes:].sum()) == 0
+        for chunks in (2, 4, 8):
+            print(f"[gpu-case] plain copy {nbytes} B, {chunks} KiB per wave", flush=True)
+            dst.zero_()
+            assert lib.bench_plain_copy_chunks(src.data_ptr(), dst.data_ptr(), nbytes, chunks,
+                                               sh) == 0
+            torch.cuda.synchronize()
+            assert torch.equal(dst[:nbytes], src) and int(dst[nbytes:].sum()) == 0
     lib.bench_plain_read.argtypes = [vp, vp, i64, ctypes.c_uint32, vp]
     lib.bench_plain_write.argtypes = [vp, i64, ctypes.c_uint32, vp]
     for nbytes in (16, 4096, 4112, (1 << 20) + 4080):

@@ -570,12 +570,13 @@ def test_copy_narrow_and_packed_rows(row, stride, ptr_off, idx64):
 
 
 @pytest.mark.parametrize("row,tokens", [(1040, 25000), (1000, 26000), (500, 52000), (2048, 12800),
-                                        (2048, 12000)])
-def test_copy_one_and_eight_token_waves_around_the_launch_size_split(row, tokens):
-    """Copies that read more than 48 MiB of rows move one token per wave,
-    smaller ones eight: each lane width (16, 8, 4 bytes) on the one-token
-    side, and 2 KiB rows just past the split, with bad tokens, every byte
-    against the oracle."""
+                                        (2048, 12000), (1000, 4500), (500, 9000), (2048, 1600),
+                                        (2048, 1500)])
+def test_copy_one_and_eight_token_waves_around_the_launch_size_splits(row, tokens):
+    """Copies that read between 6 and 48 MiB of rows move eight tokens per
+    wave, others one: each lane width (16, 8, 4 bytes) on both sides, and
+    2 KiB rows next to both splits, with bad tokens, every byte against the
+    oracle."""
     rng = np.random.Generator(np.random.PCG64(row * 7 + tokens))
     slots = 1 << 16 if row * (1 << 16) < (1 << 27) else 1 << 15
     slots = max(slots, tokens + 1024)
