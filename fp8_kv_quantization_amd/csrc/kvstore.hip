@@ -17,11 +17,14 @@
 //   * one 64-lane wave per (token, K or V, slice of the row); each lane
 //     loads 16 B per access (dwordx4), so one wave access
 //     covers 1 KiB of consecutive row bytes; copy rows or pointers aligned
-//     only to 8 or 4 bytes use 8- or 4-byte lanes, and copy rows that need at
-//     most 32 lanes are packed several to a wave;
+//     only to 8 or 4 bytes use 8- or 4-byte lanes, copy rows that need at
+//     most 32 lanes are packed several to a wave, and copy launches of 6-48
+//     MiB give each wave 8 tokens (see copy_tokens_per_wave);
 //   * every load of a wave (all its 1 KiB chunks) is issued before the
 //     index is needed: the source address does not depend on the index, so the
-//     index fetch overlaps the data fetch instead of preceding it;
+//     index fetch overlaps the data fetch instead of preceding it (the copy
+//     kernels are written so that the compiler keeps that order; see
+//     loaded() and indices_after_row_loads());
 //   * the row base addresses are wave-uniform 64-bit values (scalar registers)
 //     and the per-lane offset is a 32-bit vector register;
 //   * copy: cache rows are written with non-temporal stores, and residency is
