@@ -322,6 +322,37 @@ def test_index_stride(kind):
     assert_cache_equal(vc, ovc, "v_cache")
 
 
+def test_eight_token_waves_with_int64_strided_indices_and_padded_rows():
+    """A copy in the 6-48 MiB range (8 tokens per wave): int64 indices read
+    at a stride of 3, 1000-byte rows (8-byte lanes) at a padded input stride,
+    a batch that leaves the last wave and block partly empty, bad tokens in
+    several waves; every byte against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(2024))
+    T, row, stride, slots = 4507, 1000, 1048, 8192
+    kb = rng.integers(0, 256, (T, stride), dtype=np.uint8)
+    vb = rng.integers(0, 256, (T, stride), dtype=np.uint8)
+    idx = rng.permutation(slots)[:T].astype(np.int64)
+    for t in (0, 9, 4000, T - 1):
+        idx[t] = -1 - t
+    strided = np.full(T * 3, 7, dtype=np.int64)
+    strided[::3] = idx
+    c = kvgen.Case(name="tok8_i64", kind="copy", src_dtype="bf16", num_tokens=T, num_heads=1,
+                   head_dim=row // 2, in_stride_elems=stride // 2, k=kb.view(np.uint16),
+                   v=vb.view(np.uint16), indices=idx, idx_dtype="i64", slots=slots)
+    assert 6 << 20 < 2 * T * row <= 48 << 20
+    kc = sentinel_cache(slots, row)
+    vc = sentinel_cache(slots, row)
+    _say(f"copy 8-token waves, int64 stride 3, T={T}")
+    assert run_copy(c, kc, vc, idx_dev=to_dev(strided), idx_stride=3) == kv.OK
+    assert check_flag() == (kv.ERR_OOB, 0, 4)
+    okc = np.full((slots, row), 0xFF, dtype=np.uint8)
+    ovc = np.full_like(okc, 0xFF)
+    assert oracle.copy(kb, vb, okc, ovc, idx, row_bytes=row, k_stride=stride, v_stride=stride,
+                       cache_stride=row, size_limit=slots) == (T - 4, 0, 4)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
+
+
 def test_empty_batch_touches_nothing():
     c = kvgen.workload(1)
     kc = sentinel_cache(c.slots, c.row_bytes)
