@@ -828,13 +828,17 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
     if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
     // Per head, one lane per group writes its scale: the first of each
     // head's gph lanes (for gph = 128, lane 0 of the pass), for the head of
-    // each of its two groups.
+    // each of its two groups; non-temporal (18.55-18.61 against 18.68-18.97
+    // us with default-policy stores on the 16384-token workload).
     if constexpr (kPerHead) {
       if (gph > kWave) {
-        if (lane == 0) *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa[j];
+        if (lane == 0)
+          __builtin_nontemporal_store(sa[j], reinterpret_cast<float*>(scales + (g >> gsh) * s_head));
       } else if ((lane & (gph - 1)) == 0) {
-        *reinterpret_cast<float*>(scales + (g >> gsh) * s_head) = sa[j];
-        if (has_b) *reinterpret_cast<float*>(scales + ((g + kWave) >> gsh) * s_head) = sb[j];
+        __builtin_nontemporal_store(sa[j], reinterpret_cast<float*>(scales + (g >> gsh) * s_head));
+        if (has_b)
+          __builtin_nontemporal_store(
+              sb[j], reinterpret_cast<float*>(scales + ((g + kWave) >> gsh) * s_head));
       }
     }
   }
