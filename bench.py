@@ -258,7 +258,7 @@ def main():
 
     roofline = {
         "bound": "hbm",
-        "kernel": "kvstore_copy_kernel<16, 2, int> (prefill copy)",
+        "kernel": "kvstore_copy_kernel<16, 2, 1, int> (prefill copy)",
         "achieved": round(b3 / (copy_us * 1e-6) / 1e9, 1),
         "peak": PEAK_HBM_GBS,
         "unit": "GB/s",
