@@ -773,13 +773,16 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
   }
 
   const bool in_range = loc >= 0 && loc < p.size_limit;
+  // A rejected index addresses nothing: slot 0 stands in for it, so that no
+  // offset below is formed from an arbitrary 64-bit value.
+  const int64_t slot = in_range ? loc : 0;
   int64_t page, off;
   if (p.page_shift >= 0) {
-    page = loc >> p.page_shift;
-    off = loc & (p.page_size - 1);
+    page = slot >> p.page_shift;
+    off = slot & (p.page_size - 1);
   } else {
-    page = loc / p.page_size;
-    off = loc - page * p.page_size;
+    page = slot / p.page_size;
+    off = slot - page * p.page_size;
   }
   uint8_t* scales = is_v ? d.v_scales + page * d.vs_stride_page + off * d.vs_stride_offset
                          : d.k_scales + page * d.ks_stride_page + off * d.ks_stride_offset;
@@ -798,8 +801,9 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
     // The token scales of the block's waves (consecutive tokens) go through
     // LDS to wave 0, which stores them with one instruction: where the tokens
     // sit in consecutive slots the scales leave as one memory request instead
-    // of one per wave (two waves: 18.1 against 18.7 us on the 16384-token FP8
-    // workload; per-head scales measured no gain).  Every wave reaches the
+    // of one per wave (16384-token FP8 workload: 17.97 us with blocks of four
+    // waves, 18.08 with two, 18.15 with eight, 18.6-18.7 with a store per
+    // wave; per-head scales measured no gain).  Every wave reaches the
     // barrier.
     __shared__ float s_val[kDynWavesPerBlock];
     __shared__ float* s_at[kDynWavesPerBlock];
