@@ -534,6 +534,19 @@ __device__ __forceinline__ int64_t slot_offset(const Fp8Params& p, int64_t loc, 
   return page * c_page + off * c_offset;
 }
 
+// How the FP8 stores load their rows.  Loads under a branch per group (zeros
+// past the row) suit one pass and bf16 rows of several passes: the compiler
+// keeps every load ahead of the first wait.  For fp16 rows of several passes
+// it issues only the first two loads before waiting on them, one memory
+// latency after another, so there every lane loads (a group past the row
+// reads the row's last group and stores nothing) and the values are pinned
+// after the last load.  16384 tokens of 16x128 fp16: static store 37.41 ->
+// 37.07 us, per-token scales 39.74 -> 38.78; 8192 tokens of 32x128 fp16 with
+// per-token-head scales 44.95 -> 41.11.  The same form measured 0.9 us
+// slower for 16x128 bf16 rows and 0.3 us slower for one pass.
+template <int kPasses, bool kFp16>
+constexpr bool kUnconditionalLoads = kPasses > 1 && kFp16;
+
 // Grid: x = ceil(batch / kWavesPerBlock), one wave per token; y = 2 * slices:
 // bit 0 selects K (0) or V (1), the rest the slice of kPasses * 64 units.
 // K and V of a token go to separate waves: twice the waves of half the size
@@ -558,19 +571,38 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
   const uint32_t groups_per_head = 2u * p.units_per_head;
   u32x4 a[kPasses], b[kPasses];
   uint32_t da[kPasses], db[kPasses];
+  if constexpr (kUnconditionalLoads<kPasses, kFp16>) {
 #pragma unroll
-  for (int i = 0; i < kPasses; ++i) {
-    const uint32_t g = (slice * kPasses + i) * (2u * kWave) + lane;
-    a[i] = u32x4{0u, 0u, 0u, 0u};
-    b[i] = u32x4{0u, 0u, 0u, 0u};
-    uint32_t so;
-    if (g < groups) {
-      group_offsets<kFlat>(g, groups_per_head, t.src_head, t.c_head, &so, &da[i]);
+    for (int i = 0; i < kPasses; ++i) {
+      const uint32_t g = (slice * kPasses + i) * (2u * kWave) + lane;
+      uint32_t so;
+      group_offsets<kFlat>(g < groups ? g : groups - 1, groups_per_head, t.src_head, t.c_head, &so,
+                           &da[i]);
       a[i] = load16(t.src, so);
-    }
-    if (g + kWave < groups) {
-      group_offsets<kFlat>(g + kWave, groups_per_head, t.src_head, t.c_head, &so, &db[i]);
+      group_offsets<kFlat>(g + kWave < groups ? g + kWave : groups - 1, groups_per_head,
+                           t.src_head, t.c_head, &so, &db[i]);
       b[i] = load16(t.src, so);
+    }
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+      loaded(a[i]);
+      loaded(b[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPasses; ++i) {
+      const uint32_t g = (slice * kPasses + i) * (2u * kWave) + lane;
+      a[i] = u32x4{0u, 0u, 0u, 0u};
+      b[i] = u32x4{0u, 0u, 0u, 0u};
+      uint32_t so;
+      if (g < groups) {
+        group_offsets<kFlat>(g, groups_per_head, t.src_head, t.c_head, &so, &da[i]);
+        a[i] = load16(t.src, so);
+      }
+      if (g + kWave < groups) {
+        group_offsets<kFlat>(g + kWave, groups_per_head, t.src_head, t.c_head, &so, &db[i]);
+        b[i] = load16(t.src, so);
+      }
     }
   }
 
@@ -699,7 +731,7 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t w = threadIdx.x / kWave;
   const uint32_t i = wave_uniform(blockIdx.x * kDynWavesPerBlock + w);
-  // Per token, the waves of a block meet at a barrier before their stores,
+  // Per token, the waves of a block meet at a barrier before the scale store,
   // so a wave past the batch works on the last token and stores nothing.
   const bool valid = i < p.batch;
   if (kPerHead && !valid) return;
@@ -713,19 +745,44 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
 
   u32x4 a[kPasses], b[kPasses];
   uint32_t da[kPasses], db[kPasses];
+  if constexpr (kUnconditionalLoads<kPasses, kFp16>) {
 #pragma unroll
-  for (int j = 0; j < kPasses; ++j) {
-    const uint32_t g = j * (2u * kWave) + lane;
-    a[j] = u32x4{0u, 0u, 0u, 0u};
-    b[j] = u32x4{0u, 0u, 0u, 0u};
-    uint32_t so;
-    if (g < groups) {
-      group_offsets<kFlat>(g, gph, t.src_head, t.c_head, &so, &da[j]);
+    for (int j = 0; j < kPasses; ++j) {
+      const uint32_t g = j * (2u * kWave) + lane;
+      uint32_t so;
+      group_offsets<kFlat>(g < groups ? g : groups - 1, gph, t.src_head, t.c_head, &so, &da[j]);
       a[j] = load16(t.src, so);
-    }
-    if (g + kWave < groups) {
-      group_offsets<kFlat>(g + kWave, gph, t.src_head, t.c_head, &so, &db[j]);
+      group_offsets<kFlat>(g + kWave < groups ? g + kWave : groups - 1, gph, t.src_head, t.c_head,
+                           &so, &db[j]);
       b[j] = load16(t.src, so);
+    }
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+      loaded(a[j]);
+      loaded(b[j]);
+    }
+    // groups past the row take no part in the maxima
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+      const uint32_t g = j * (2u * kWave) + lane;
+      if (g >= groups) a[j] = u32x4{0u, 0u, 0u, 0u};
+      if (g + kWave >= groups) b[j] = u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+      const uint32_t g = j * (2u * kWave) + lane;
+      a[j] = u32x4{0u, 0u, 0u, 0u};
+      b[j] = u32x4{0u, 0u, 0u, 0u};
+      uint32_t so;
+      if (g < groups) {
+        group_offsets<kFlat>(g, gph, t.src_head, t.c_head, &so, &da[j]);
+        a[j] = load16(t.src, so);
+      }
+      if (g + kWave < groups) {
+        group_offsets<kFlat>(g + kWave, gph, t.src_head, t.c_head, &so, &db[j]);
+        b[j] = load16(t.src, so);
+      }
     }
   }
   // Every lane takes part in the lane reductions below (groups past the row
@@ -797,54 +854,56 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
     sb[j] = dyn_scale(mag_to_float<kFp16>(mb[j]));
   }
 
+  // Per token, the scales of the block's waves (consecutive tokens) go
+  // through LDS to wave 0, which stores them with one instruction after the
+  // rows: where the tokens sit in consecutive slots the scales leave as one
+  // memory request instead of one per wave (16384-token FP8 workload: 17.97
+  // us with blocks of four waves, 18.08 with two, 18.15 with eight, 18.6-18.7
+  // with a store per wave; the barrier after the row stores rather than
+  // before them 17.84 against 17.99; per-head scales measured no gain).
+  // Every wave of the block reaches the barrier.
+  __shared__ float s_val[kDynWavesPerBlock];
+  __shared__ float* s_at[kDynWavesPerBlock];
   if constexpr (!kPerHead) {
-    // The token scales of the block's waves (consecutive tokens) go through
-    // LDS to wave 0, which stores them with one instruction: where the tokens
-    // sit in consecutive slots the scales leave as one memory request instead
-    // of one per wave (16384-token FP8 workload: 17.97 us with blocks of four
-    // waves, 18.08 with two, 18.15 with eight, 18.6-18.7 with a store per
-    // wave; per-head scales measured no gain).  Every wave reaches the
-    // barrier.
-    __shared__ float s_val[kDynWavesPerBlock];
-    __shared__ float* s_at[kDynWavesPerBlock];
     if (lane == 0) {
       s_val[w] = sa[0];
       s_at[w] = valid && in_range ? reinterpret_cast<float*>(scales) : nullptr;
     }
+  }
+  if (valid && !in_range && lane == 0 && !is_v) report_bad_token(token);
+  if (valid && in_range) {
+    const __amdgpu_buffer_rsrc_t dst = row_rsrc(t.cache + page * t.c_page + off * t.c_offset);
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+      const uint32_t g = j * (2u * kWave) + lane;
+      if (g >= groups) continue;
+      const bool has_b = g + kWave < groups;
+      const float ia = 1.0f / sa[j], ib = 1.0f / sb[j];
+      const u32x4 q = quantize16_checked<kFp16, false>(a[j], b[j], ia, ib);
+      store8_sc1(dst, da[j], u32x2{q.x, q.y});
+      if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
+      // Per head, one lane per group writes its scale: the first of each
+      // head's gph lanes (for gph = 128, lane 0 of the pass), for the head of
+      // each of its two groups; non-temporal (18.55-18.61 against 18.68-18.97
+      // us with default-policy stores on the 16384-token workload).
+      if constexpr (kPerHead) {
+        if (gph > kWave) {
+          if (lane == 0)
+            __builtin_nontemporal_store(sa[j],
+                                        reinterpret_cast<float*>(scales + (g >> gsh) * s_head));
+        } else if ((lane & (gph - 1)) == 0) {
+          __builtin_nontemporal_store(sa[j], reinterpret_cast<float*>(scales + (g >> gsh) * s_head));
+          if (has_b)
+            __builtin_nontemporal_store(
+                sb[j], reinterpret_cast<float*>(scales + ((g + kWave) >> gsh) * s_head));
+        }
+      }
+    }
+  }
+  if constexpr (!kPerHead) {
     __syncthreads();
     if (w == 0 && lane < (uint32_t)kDynWavesPerBlock && s_at[lane] != nullptr)
       *s_at[lane] = s_val[lane];
-  }
-  if (!valid) return;
-  if (!in_range) {
-    if (lane == 0 && !is_v) report_bad_token(token);
-    return;
-  }
-  const __amdgpu_buffer_rsrc_t dst = row_rsrc(t.cache + page * t.c_page + off * t.c_offset);
-#pragma unroll
-  for (int j = 0; j < kPasses; ++j) {
-    const uint32_t g = j * (2u * kWave) + lane;
-    if (g >= groups) continue;
-    const bool has_b = g + kWave < groups;
-    const float ia = 1.0f / sa[j], ib = 1.0f / sb[j];
-    const u32x4 q = quantize16_checked<kFp16, false>(a[j], b[j], ia, ib);
-    store8_sc1(dst, da[j], u32x2{q.x, q.y});
-    if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
-    // Per head, one lane per group writes its scale: the first of each
-    // head's gph lanes (for gph = 128, lane 0 of the pass), for the head of
-    // each of its two groups; non-temporal (18.55-18.61 against 18.68-18.97
-    // us with default-policy stores on the 16384-token workload).
-    if constexpr (kPerHead) {
-      if (gph > kWave) {
-        if (lane == 0)
-          __builtin_nontemporal_store(sa[j], reinterpret_cast<float*>(scales + (g >> gsh) * s_head));
-      } else if ((lane & (gph - 1)) == 0) {
-        __builtin_nontemporal_store(sa[j], reinterpret_cast<float*>(scales + (g >> gsh) * s_head));
-        if (has_b)
-          __builtin_nontemporal_store(
-              sb[j], reinterpret_cast<float*>(scales + ((g + kWave) >> gsh) * s_head));
-      }
-    }
   }
 }
 

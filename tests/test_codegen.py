@@ -9,10 +9,10 @@ after another (copies of 3 and 4 KiB rows ran 30% slower that way).  A
 kernel that fails here has changed shape, not just timing.
 
 Covered: every instantiation of the row copy, of the packed small-row copy,
-of the one-pass FP8 store and of the one-pass dynamic-scale store.  The
-multi-pass fp16 FP8 forms issue half of their loads after a wait and time
-the same as with all loads first (their waves run at full occupancy), so
-the multi-pass forms are not held to it.
+of the FP8 store and of the dynamic-scale store (one pass or several, bf16
+or fp16).  Left alone, the compiler issued only the first two loads of an
+fp16 row of several passes before waiting on them (8192 tokens of 32x128
+fp16 with per-token-head scales ran 9% slower than bf16 of the same size).
 """
 import os
 import re
@@ -28,8 +28,8 @@ import _build  # noqa: E402
 COVERED = (
     r"kvstore_copy_kernelILi\d+ELi\d+ELi\d+E[il]E",
     r"kvstore_copy_packed_kernelILi\d+E[il]E",
-    r"kvstore_fp8_paged_kernelILi1ELb[01]ELb[01]ELb[01]E[il]E",
-    r"kvstore_fp8_dynamic_kernelILi1ELb[01]ELb[01]ELb[01]E[il]E",
+    r"kvstore_fp8_paged_kernelILi\d+ELb[01]ELb[01]ELb[01]E[il]E",
+    r"kvstore_fp8_dynamic_kernelILi\d+ELb[01]ELb[01]ELb[01]E[il]E",
 )
 
 
@@ -76,8 +76,9 @@ def test_every_row_load_is_in_flight_before_the_first_wait(asm):
     ks = kernels(asm)
     covered = {k: b for k, b in ks.items() if any(re.search(p, k) for p in COVERED)}
     # 3 lane widths x (4 chunk counts + 2 with several tokens per wave) x 2
-    # index types; packed: 3 lane widths x 2 index types; 16 + 16 FP8 forms
-    assert len(covered) == 36 + 6 + 16 + 16, sorted(covered)
+    # index types; packed: 3 lane widths x 2 index types; FP8: 1 or 2 passes
+    # x 16 forms; dynamic: 1, 2 or 4 passes x 16 forms
+    assert len(covered) == 36 + 6 + 32 + 48, sorted(covered)
     bad = {}
     for name, body in covered.items():
         before, total = loads_before_first_wait(body)

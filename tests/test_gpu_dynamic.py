@@ -96,14 +96,21 @@ def test_dynamic_full_size(per_head):
                                              (32, 128, (False, True)), (2, 576, (False,)),
                                              (4, 1024, (False, True)), (2, 32, (True,)),
                                              (4, 256, (False, True)), (8, 512, (False, True))])
-def test_dynamic_head_shapes(heads, dim, modes):
+@pytest.mark.parametrize("src", ["bf16", "fp16"])
+def test_dynamic_head_shapes(heads, dim, modes, src):
+    # Rows of one to four passes, some ending inside a pass (2 x 576), in
+    # both source formats (fp16 rows of several passes load every group,
+    # clamped to the row, and zero those past it).
     rng = np.random.Generator(np.random.PCG64(heads * 7 + dim))
     T, P, pages = 150, 16, 12
     x = rng.standard_normal((2, T, heads * dim), dtype=np.float32)
     x *= np.exp(rng.standard_normal((2, T, heads, 1), dtype=np.float32) * 3).repeat(dim, 3).reshape(x.shape)
-    bits = kvgen._round_f32_to_bf16_bits(x)
+    if src == "bf16":
+        bits = kvgen._round_f32_to_bf16_bits(x)
+    else:
+        bits = np.clip(x, -60000, 60000).astype(np.float16).view(np.uint16)
     idx = rng.permutation(P * pages)[:T].astype(np.int32)
-    c = kvgen.Case(name=f"h{heads}d{dim}", kind="fp8", src_dtype="bf16", num_tokens=T,
+    c = kvgen.Case(name=f"h{heads}d{dim}", kind="fp8", src_dtype=src, num_tokens=T,
                    num_heads=heads, head_dim=dim, in_stride_elems=heads * dim, k=bits[0],
                    v=bits[1], indices=idx, idx_dtype="i32", slots=P * pages, page_size=P)
     for per_head in modes:

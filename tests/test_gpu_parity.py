@@ -162,6 +162,28 @@ def test_fp8_options(src, scales, i64):
     fp8_parity(_fp8_case(src=src, scales=scales, i64=i64))
 
 
+@pytest.mark.parametrize("heads,dim", [(16, 128), (5, 272), (24, 256)])
+@pytest.mark.parametrize("src", ["bf16", "fp16"])
+def test_fp8_rows_of_several_passes(heads, dim, src):
+    # 2048 elements (two whole passes), 1360 (the second pass ends inside the
+    # row's last 64 groups) and 6144 (two passes in each of three grid
+    # slices); fp16 rows of several passes load every group, clamped to the
+    # row, and store only those inside it.
+    rng = np.random.Generator(np.random.PCG64(heads * 31 + dim))
+    T, P, pages = 200, 16, 16
+    x = rng.standard_normal((2, T, heads * dim), dtype=np.float32) * 40
+    if src == "bf16":
+        bits = kvgen._round_f32_to_bf16_bits(x)
+    else:
+        bits = x.astype(np.float16).view(np.uint16)
+    idx = rng.permutation(P * pages)[:T].astype(np.int32)
+    c = kvgen.Case(name=f"fp8_h{heads}d{dim}", kind="fp8", src_dtype=src, num_tokens=T,
+                   num_heads=heads, head_dim=dim, in_stride_elems=heads * dim, k=bits[0],
+                   v=bits[1], indices=idx, idx_dtype="i32", slots=P * pages, page_size=P,
+                   inv_k_bits=kvgen.INV_K_BITS, inv_v_bits=kvgen.INV_V_BITS)
+    fp8_parity(c)
+
+
 @pytest.mark.parametrize("page_size", [48, 16, 1])
 def test_fp8_page_sizes(page_size):
     fp8_parity(_fp8_case(page_size=page_size))
