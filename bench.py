@@ -56,6 +56,12 @@ def parse():
     ap.add_argument("--copy-patterns", action="store_true",
                     help="only time the prefill copy over four destination patterns (12 launches "
                          "each: 2 untimed, 10 timed; for counter runs) and print that as the line")
+    ap.add_argument("--copy-extents", action="store_true",
+                    help="only time the prefill copy with its 16-slot runs drawn from cache "
+                         "extents of 64 MiB .. 4 GiB per tensor (12 launches each, for counter "
+                         "runs, then --extent-windows timed windows) and print that as the line")
+    ap.add_argument("--extent-windows", type=int, default=3,
+                    help="timed 50-call windows per extent after the 12 launches (0: none)")
     return ap.parse_args()
 
 
@@ -168,6 +174,21 @@ def main():
         print(json.dumps(out), flush=True)
         return
 
+    if args.copy_extents:
+        named = {f"{mib}MiB": kvgen.extent_index_sets(c3, mib << 20, S) for mib in kvgen.EXTENT_MIB}
+        sample = bench_index_sets(kv, torch, c3, k3, v3, kc3, vc3, S, sh, named,
+                                  windows=1, n=10, warm=2)
+        out = {"metric": "prefill copy launch time by the extent its 16-slot runs are drawn from",
+               "unit": "us", "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+               "config": {"workload": "prefill copy (32768 tok, 8x128 bf16, int32, 2^21 slots), "
+                                      "index sets replaced per extent", "rotation_sets": S},
+               "counter_sample_12_launches": sample}
+        if args.extent_windows > 0:
+            out["extents"] = bench_index_sets(kv, torch, c3, k3, v3, kc3, vc3, S, sh, named,
+                                              windows=args.extent_windows, n=50, warm=100)
+        print(json.dumps(out), flush=True)
+        return
+
     if args.calib_copy_mib:
         n = args.calib_copy_mib << 20
         a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
@@ -223,10 +244,13 @@ def main():
     fp8_us = fp8_ms_total * 1e3 / K
     value = (b3 + b4) / (ms_per_step * 1e-3) / 1e9
 
-    hot = patterns = None
+    hot = patterns = extents = None
     if not args.no_next:
         hot = bench_hot(torch, copy_call, fp8_call, b3, b4)
         patterns = bench_patterns(kv, torch, kvgen, c3, k3, v3, kc3, vc3, S, sh)
+        extents = bench_index_sets(
+            kv, torch, c3, k3, v3, kc3, vc3, S, sh,
+            {f"{mib}MiB": kvgen.extent_index_sets(c3, mib << 20, S) for mib in kvgen.EXTENT_MIB})
 
     next_rows = None
     if not args.no_next:
@@ -316,6 +340,7 @@ def main():
         "plain_kernels_same_bytes": plain,
         "serial_bound": bound,
         "copy_destination_patterns": patterns,
+        "copy_destination_extents": extents,
         "hot_non_rotated": hot,
         "cpu_baseline": cpu,
     }
@@ -362,16 +387,23 @@ def bench_patterns(kv, torch, kvgen, c3, k3, v3, kc3, vc3, S, sh, windows=3, n=5
     """The prefill copy (same rows, same library call) with its index sets
     replaced by four destination patterns (kvgen.pattern_index_sets):
     contiguous slots, 16-slot runs inside a 64 MiB extent, the workload's
-    16-slot runs over the 4 GiB cache, single slots over the cache.  Average
-    launch time per pattern (median of `windows` windows of n calls after
-    `warm` calls, HIP events on the launch stream), rotated over S sets."""
+    16-slot runs over the 4 GiB cache, single slots over the cache."""
+    named = {pat: kvgen.pattern_index_sets(c3, pat, S) for pat in kvgen.DEST_PATTERNS}
+    return bench_index_sets(kv, torch, c3, k3, v3, kc3, vc3, S, sh, named, windows, n, warm)
+
+
+def bench_index_sets(kv, torch, c3, k3, v3, kc3, vc3, S, sh, named, windows=3, n=50, warm=200):
+    """The prefill copy (same rows, same library call) with its index sets
+    replaced by each entry of `named` (S host index arrays per name), in
+    order.  Average launch time per entry (median of `windows` windows of n
+    calls after `warm` calls, HIP events on the launch stream), rotated over
+    the S sets."""
     import numpy as np
     R, T = c3.row_bytes, c3.num_tokens
     dev = k3[0].device
     out = {}
-    for pat in kvgen.DEST_PATTERNS:
-        idx = [torch.from_numpy(np.ascontiguousarray(a)).to(dev)
-               for a in kvgen.pattern_index_sets(c3, pat, S)]
+    for pat, sets in named.items():
+        idx = [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in sets]
 
         def call(s):
             st = kv.kvstore_copy(k3[s].data_ptr(), v3[s].data_ptr(), kc3.data_ptr(), vc3.data_ptr(),

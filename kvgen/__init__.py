@@ -283,3 +283,36 @@ def pattern_index_sets(case: Case, pattern: str, count: int, seed: int = 4242) -
         pick = rng.permutation(case.slots)[:count * T].astype(np.int64)
         return [pick[s * T:(s + 1) * T].astype(dt) for s in range(count)]
     raise ValueError(f"unknown destination pattern {pattern!r}")
+
+
+EXTENT_MIB = (64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def extent_index_sets(case: Case, extent_bytes: int, count: int, seed: int = 4343) -> list:
+    """``count`` pairwise-disjoint index arrays for ``case`` that keep its
+    scheme (runs of ``index_page`` consecutive slots, whole runs in random
+    order) but draw each set's runs from a cache extent of ``extent_bytes``
+    per tensor, to see how the store's time depends on how densely the
+    written runs sit in memory.  While ``count`` extents fit in the cache and
+    one extent is smaller than the runs of all sets together, set s takes
+    its runs from its own extent [s*E, (s+1)*E); otherwise the sets share the
+    extent [0, E), each with its own runs."""
+    run = case.extra.get("index_page", 1)
+    T, dt = case.num_tokens, case.indices.dtype
+    need = -(-T // run)
+    ext_runs = extent_bytes // (run * case.row_bytes)
+    all_runs = case.slots // run
+    own = ext_runs * count <= all_runs and ext_runs < need * count
+    if ext_runs < need or (not own and (need * count > ext_runs or ext_runs > all_runs)):
+        raise ValueError("extent does not fit the sets")
+    rng = np.random.Generator(np.random.PCG64(seed))
+    t = np.arange(T, dtype=np.int64)
+    out = []
+    shared = None if own else rng.permutation(ext_runs)
+    for s in range(count):
+        if own:
+            p = rng.permutation(ext_runs)[:need].astype(np.int64) + s * ext_runs
+        else:
+            p = shared[s * need:(s + 1) * need].astype(np.int64)
+        out.append((p[t // run] * run + t % run).astype(dt))
+    return out

@@ -130,3 +130,65 @@ def test_disjoint_index_sets(cases, n, count):
         t = np.arange(c.num_tokens)
         for s in sets:
             assert np.array_equal(s.astype(np.int64) % page, t % page)
+
+
+def _check_runs(case, s):
+    """Index array s keeps the case's scheme: tokens t of one run go to
+    consecutive slots of one whole run, each run used once."""
+    run = case.extra["index_page"]
+    t = np.arange(case.num_tokens)
+    s = s.astype(np.int64)
+    assert np.array_equal(s % run, t % run)
+    starts = (s // run)[::run]
+    assert np.array_equal(s // run, np.repeat(starts, run)[:case.num_tokens])
+    assert np.unique(starts).size == starts.size
+
+
+@pytest.mark.parametrize("pattern", kvgen.DEST_PATTERNS)
+def test_pattern_index_sets(cases, pattern):
+    c = cases[3]
+    sets = kvgen.pattern_index_sets(c, pattern, 8)
+    allidx = np.concatenate([s.astype(np.int64) for s in sets])
+    assert np.unique(allidx).size == 8 * c.num_tokens
+    assert allidx.min() >= 0 and allidx.max() < c.slots
+    assert all(s.dtype == c.indices.dtype for s in sets)
+    T = c.num_tokens
+    if pattern == "contiguous":
+        for k, s in enumerate(sets):
+            assert np.array_equal(s, np.arange(k * T, (k + 1) * T))
+    elif pattern == "runs16_in_64MiB":
+        for k, s in enumerate(sets):
+            _check_runs(c, s)
+            # set k fills its own 64 MiB extent exactly
+            assert np.array_equal(np.sort(s.astype(np.int64)), np.arange(k * T, (k + 1) * T))
+            assert T * c.row_bytes == 64 << 20
+    elif pattern == "workload":
+        assert np.array_equal(sets[0], c.indices)
+        for s in sets:
+            _check_runs(c, s)
+
+
+@pytest.mark.parametrize("mib", kvgen.EXTENT_MIB)
+def test_extent_index_sets(cases, mib):
+    c = cases[3]
+    E = (mib << 20) // c.row_bytes                  # slots per extent
+    sets = kvgen.extent_index_sets(c, mib << 20, 8)
+    allidx = np.concatenate([s.astype(np.int64) for s in sets])
+    assert np.unique(allidx).size == 8 * c.num_tokens
+    assert allidx.min() >= 0 and allidx.max() < c.slots
+    own = 8 * E <= c.slots and E < 8 * c.num_tokens
+    for k, s in enumerate(sets):
+        _check_runs(c, s)
+        lo, hi = (k * E, (k + 1) * E) if own else (0, E)
+        assert s.min() >= lo and s.max() < hi, (mib, k)
+    # the runs spread over the extent: the written slots span most of it
+    span = allidx.max() - allidx.min() + 1 if not own else sets[0].max() - sets[0].min() + 1
+    assert span > 0.9 * E
+
+
+def test_extent_index_sets_refuses_what_does_not_fit(cases):
+    c = cases[3]
+    with pytest.raises(ValueError):
+        kvgen.extent_index_sets(c, 32 << 20, 8)    # smaller than one set's runs
+    with pytest.raises(ValueError):
+        kvgen.extent_index_sets(c, 8 << 30, 8)     # larger than the cache
