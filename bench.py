@@ -267,7 +267,10 @@ def main():
     plain = bound = None
     if not args.no_next:
         plain = bench_plain_kernels(torch, dev, b3, c4, S)
-        bound = bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, copy_sets=(kc3, vc3, i3))
+        bound = bench_serial_bound(
+            torch, dev, c3, c4, copy_us, fp8_us,
+            dest_sets={"prefill_copy": (kc3, vc3, i3, R3, c3.slots),
+                       "fp8_paged": (kc4, vc4, i4, R4, c4.slots)})
 
     # Launch-bound decode-size figures last: the idle gaps of their
     # single-call latency loop leave the GPU slow to return to full speed for
@@ -480,7 +483,7 @@ def plain_copy_us(torch, dev, nbytes, S, n=50):
     return best
 
 
-def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, copy_sets=None, n=50):
+def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, dest_sets=None, n=50):
     """Same-run attainable bound for the step's two kernels.  HBM serves a
     kernel's read and write streams one after the other, so a kernel that
     reads r bytes and writes w bytes takes at least r/R + w/W, with R and W
@@ -488,10 +491,11 @@ def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, copy_sets=None, n=50
     (bench_plain.hip, each in the fastest form measured).  Two forms: R and W
     measured at the kernel's own byte counts (each plain launch pays its own
     launch ramp, so this bound is the looser one) and at 1 GiB per launch
-    (near the asymptotic rates).  With `copy_sets` ((k_cache, v_cache, S
-    device index arrays) of the prefill copy), the copy also gets the bound
-    of its own destinations: the read-only time plus a write-only kernel
-    that writes its rows to the same slots (no reads at all)."""
+    (near the asymptotic rates).  With `dest_sets` ({kernel: (k_cache,
+    v_cache, S device index arrays, row bytes, slots)}; caches whose slot
+    row is `row bytes` long at a stride of `row bytes`), each kernel also
+    gets the bound of its own destinations: the read-only time plus a
+    write-only kernel that writes its rows to the same slots (no reads)."""
     lib = _plain_lib()
     if lib is None:
         return None
@@ -547,32 +551,32 @@ def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, copy_sets=None, n=50
                      "frac_of_bound_at_size": round((tr + tw) / k_us, 4),
                      "bound_us_asymptotic": round(b_inf, 3),
                      "frac_of_bound_asymptotic": round(b_inf / k_us, 4)}
-    if copy_sets is not None:
-        kc, vc, idx = copy_sets
-        R, T = c3.row_bytes, c3.num_tokens
-
-        def scatter_us(sets, cap):
+    if dest_sets is not None:
+        def scatter_us(kc, vc, sets, T, R, slots, cap):
             def call(s):
                 if lib.bench_plain_scatter_write(kc.data_ptr(), vc.data_ptr(), sets[s].data_ptr(),
-                                                 T, R, R, c3.slots, s, cap, sh):
+                                                 T, R, R, slots, s, cap, sh):
                     raise RuntimeError("bench_plain_scatter_write failed")
             return time_calls(torch, call, len(sets), n=n)
 
-        # fastest of uncapped and of the copy's own residency (12 waves per CU)
-        wl = min(scatter_us(idx, cap) for cap in (0, 12))
-        cont = [torch.arange(s * T, (s + 1) * T, dtype=torch.int32, device=dev)
-                for s in range(len(idx))]
-        ct = min(scatter_us(cont, cap) for cap in (0, 12))
-        tr = out["prefill_copy"]["read_only_us"]
-        out["prefill_copy"].update({
-            "write_only_contiguous_slots_us": round(ct, 3),
-            "write_only_workload_destinations_us": round(wl, 3),
-            "bound_us_workload_destinations": round(tr + wl, 3),
-            "frac_of_bound_workload_destinations": round((tr + wl) / copy_us, 4)})
+        for name, (kc, vc, idx, R, slots) in dest_sets.items():
+            k_us = out[name]["kernel_us"]
+            T = int(idx[0].numel())
+            # fastest of uncapped and of 12 waves per CU (the copy's residency)
+            wl = min(scatter_us(kc, vc, idx, T, R, slots, cap) for cap in (0, 12))
+            cont = [torch.arange(s * T, (s + 1) * T, dtype=torch.int32, device=dev)
+                    for s in range(len(idx))]
+            ct = min(scatter_us(kc, vc, cont, T, R, slots, cap) for cap in (0, 12))
+            tr = out[name]["read_only_us"]
+            out[name].update({
+                "write_only_contiguous_slots_us": round(ct, 3),
+                "write_only_workload_destinations_us": round(wl, 3),
+                "bound_us_workload_destinations": round(tr + wl, 3),
+                "frac_of_bound_workload_destinations": round((tr + wl) / k_us, 4)})
         out["workload_destinations"] = (
-            "write-only kernel (bench_plain_scatter_write): the copy's rows written to its own "
-            "index sets' slots with no reads, non-temporal 16-byte stores, the faster of "
-            "uncapped and 12 waves per CU; and the same into contiguous slots")
+            "write-only kernel (bench_plain_scatter_write): the kernel's rows (K and V) written "
+            "to its own index sets' slots with no reads, non-temporal 16-byte stores, the faster "
+            "of uncapped and 12 waves per CU; and the same into contiguous slots")
     return out
 
 
