@@ -164,7 +164,8 @@ def test_fp8_options(src, scales, i64):
 
 @pytest.mark.parametrize("heads,dim", [(16, 128), (5, 272), (24, 256)])
 @pytest.mark.parametrize("src", ["bf16", "fp16"])
-def test_fp8_rows_of_several_passes(heads, dim, src):
+@pytest.mark.parametrize("fmt", ["e4m3fn", "e5m2"])
+def test_fp8_rows_of_several_passes(heads, dim, src, fmt):
     # 2048 elements (two whole passes), 1360 (the second pass ends inside the
     # row's last 64 groups) and 6144 (two passes in each of three grid
     # slices); fp16 rows of several passes load every group, clamped to the
@@ -181,7 +182,15 @@ def test_fp8_rows_of_several_passes(heads, dim, src):
                    num_heads=heads, head_dim=dim, in_stride_elems=heads * dim, k=bits[0],
                    v=bits[1], indices=idx, idx_dtype="i32", slots=P * pages, page_size=P,
                    inv_k_bits=kvgen.INV_K_BITS, inv_v_bits=kvgen.INV_V_BITS)
-    fp8_parity(c)
+    _say(f"fp8 rows of several passes {heads}x{dim} {src} {fmt}")
+    kc = sentinel_cache(c.slots, c.row_elems)
+    vc = sentinel_cache(c.slots, c.row_elems)
+    assert run_fp8(c, kc, vc, fmt=fmt) == kv.OK
+    assert check_flag() == (kv.OK, -1, 0)
+    okc, ovc, st = oracle.run_case(c, fmt=fmt)
+    assert st == (T, -1, 0)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
 
 
 @pytest.mark.parametrize("page_size", [48, 16, 1])
@@ -232,7 +241,15 @@ def test_fp8_head_shapes(heads, dim):
                    num_heads=heads, head_dim=dim, in_stride_elems=heads * dim, k=bits[0],
                    v=bits[1], indices=idx, idx_dtype="i32", slots=P * pages, page_size=P,
                    inv_k_bits=kvgen.INV_K_BITS, inv_v_bits=kvgen.INV_V_BITS)
-    fp8_parity(c)
+    _say(f"fp8 rows of several passes {heads}x{dim} {src} {fmt}")
+    kc = sentinel_cache(c.slots, c.row_elems)
+    vc = sentinel_cache(c.slots, c.row_elems)
+    assert run_fp8(c, kc, vc, fmt=fmt) == kv.OK
+    assert check_flag() == (kv.OK, -1, 0)
+    okc, ovc, st = oracle.run_case(c, fmt=fmt)
+    assert st == (T, -1, 0)
+    assert_cache_equal(kc, okc, "k_cache")
+    assert_cache_equal(vc, ovc, "v_cache")
 
 
 def test_fp8_flat_and_paged_tensor_api_agree():
