@@ -293,6 +293,13 @@ def main():
         "traffic": None if traffic is None else int(traffic["copy_fetch_bytes"] + traffic["copy_write_bytes"]),
         "algorithmic_bytes": b3,
         "avg_launch_us": round(copy_us, 3),
+        # the same launch against the same-run bounds of serial_bound: plain
+        # read-only + write-only at 1 GiB, and read-only + write-only into the
+        # copy's own destinations
+        "frac_of_serial_bound": None if bound is None else
+        bound["prefill_copy"]["frac_of_bound_asymptotic"],
+        "frac_of_destination_bound": None if bound is None else
+        bound["prefill_copy"].get("frac_of_bound_workload_destinations"),
     }
     breakdown = {
         "prefill_copy": {"avg_launch_us": round(copy_us, 3), "bytes": b3,
