@@ -241,15 +241,7 @@ def test_fp8_head_shapes(heads, dim):
                    num_heads=heads, head_dim=dim, in_stride_elems=heads * dim, k=bits[0],
                    v=bits[1], indices=idx, idx_dtype="i32", slots=P * pages, page_size=P,
                    inv_k_bits=kvgen.INV_K_BITS, inv_v_bits=kvgen.INV_V_BITS)
-    _say(f"fp8 rows of several passes {heads}x{dim} {src} {fmt}")
-    kc = sentinel_cache(c.slots, c.row_elems)
-    vc = sentinel_cache(c.slots, c.row_elems)
-    assert run_fp8(c, kc, vc, fmt=fmt) == kv.OK
-    assert check_flag() == (kv.OK, -1, 0)
-    okc, ovc, st = oracle.run_case(c, fmt=fmt)
-    assert st == (T, -1, 0)
-    assert_cache_equal(kc, okc, "k_cache")
-    assert_cache_equal(vc, ovc, "v_cache")
+    fp8_parity(c)
 
 
 def test_fp8_flat_and_paged_tensor_api_agree():
