@@ -1,4 +1,4 @@
-"""Every name a test module's functions read is defined somewhere: a local,
+"""Every name the Python files' functions read is defined somewhere: a local,
 a parameter, an enclosing function's name, a module-level definition or
 import, or a builtin.  The GPU tests only run on a GPU, so a stray name in
 one (say, left behind by an edit of a neighbouring test) would otherwise
@@ -12,7 +12,10 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 MODULES = sorted(glob.glob(os.path.join(ROOT, "tests", "*.py")) +
-                 [os.path.join(ROOT, "bench.py"), os.path.join(ROOT, "__graft_entry__.py")])
+                 glob.glob(os.path.join(ROOT, "tests", "*", "*.py")) +
+                 [os.path.join(ROOT, f) for f in (
+                     "bench.py", "__graft_entry__.py", "kvgen/__init__.py", "oracle/__init__.py",
+                     "fp8_kv_quantization_amd/__init__.py", "fp8_kv_quantization_amd/_build.py")])
 
 
 def _undefined(path):
