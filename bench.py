@@ -582,8 +582,8 @@ def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, dest_sets=None, n=50
                 "frac_of_bound_workload_destinations": round((tr + wl) / k_us, 4)})
         out["workload_destinations"] = (
             "write-only kernel (bench_plain_scatter_write): the kernel's rows (K and V) written "
-            "to its own index sets' slots with no reads, non-temporal 16-byte stores, the faster "
-            "of uncapped and 12 waves per CU; and the same into contiguous slots")
+            "to its own index sets' slots with no reads, 16-byte sc1 stores, the faster of "
+            "uncapped and 12 waves per CU; and the same into contiguous slots")
     return out
 
 

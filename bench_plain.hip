@@ -34,8 +34,10 @@
 //                            for each of `tokens` int32 indices: the prefill
 //                            copy's destinations with no reads at all (one
 //                            wave per row, blocks of 2 waves, K and V over
-//                            grid z, non-temporal 16-byte stores as the copy
-//                            writes; at most `waves_per_cu` waves resident
+//                            grid z, 16-byte sc1 buffer stores: the fastest
+//                            of sc1, non-temporal and default stores with 1,
+//                            2 or 4 rows per wave; at most `waves_per_cu`
+//                            waves resident
 //                            per CU when non-zero, by a dynamic LDS
 //                            allocation the kernel never touches).  Rows
 //                            whose index lies outside [0, slots) are skipped.
@@ -154,14 +156,15 @@ __global__ __launch_bounds__(128) void plain_scatter_write(uint8_t* __restrict__
   const uint32_t lane = threadIdx.x % kWave;
   const int64_t loc = idx[t];
   if (loc < 0 || loc >= slots) return;
-  u32x4* row = reinterpret_cast<u32x4*>((blockIdx.z ? vc : kc) + (uint64_t)loc * cache_stride);
+  const __amdgpu_buffer_rsrc_t row = rsrc((blockIdx.z ? vc : kc) + (uint64_t)loc * cache_stride);
   const uint32_t salt = seed ^ (blockIdx.z ? 0x5BD1E995u : 0u);
 #pragma unroll
   for (uint32_t c = 0; c < 4; ++c) {
     if (c < chunks) {
       const uint32_t h = (t * 0x9E3779B1u + c * kWave + lane) ^ salt;
-      __builtin_nontemporal_store(u32x4{h, h ^ 0x85EBCA6Bu, h ^ 0xC2B2AE35u, h + 0x27D4EB2Fu},
-                                  row + c * kWave + lane);
+      __builtin_amdgcn_raw_buffer_store_b128(
+          u32x4{h, h ^ 0x85EBCA6Bu, h ^ 0xC2B2AE35u, h + 0x27D4EB2Fu}, row,
+          (int)((c * kWave + lane) * 16), 0, kSc1);
     }
   }
 }
