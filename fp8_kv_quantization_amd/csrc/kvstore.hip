@@ -27,10 +27,11 @@
 //     loaded() and indices_after_row_loads());
 //   * the row base addresses are wave-uniform 64-bit values (scalar registers)
 //     and the per-lane offset is a 32-bit vector register;
-//   * copy: cache rows are written with non-temporal stores, and residency is
-//     capped to about 24 KiB of loads in flight per CU (12 waves of 2 KiB
-//     rows; see copy_waves_per_cu): the rows land at scattered slots, and
-//     fewer concurrent write streams measured faster;
+//   * copy: cache rows are written with sc1 buffer stores by single-token
+//     waves of 16-byte lanes and with non-temporal stores otherwise, and
+//     residency is capped to about 24 KiB of loads in flight per CU (12
+//     waves of 2 KiB rows; see copy_waves_per_cu): the rows land at
+//     scattered slots, and fewer concurrent write streams measured faster;
 //   * fp8: the quantised rows are written with the sc1 cache policy through a
 //     per-row buffer descriptor, at full occupancy (the conversion needs the
 //     latency hiding);
