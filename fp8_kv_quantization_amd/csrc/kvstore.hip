@@ -27,11 +27,11 @@
 //     loaded() and indices_after_row_loads());
 //   * the row base addresses are wave-uniform 64-bit values (scalar registers)
 //     and the per-lane offset is a 32-bit vector register;
-//   * copy: cache rows are written with sc1 buffer stores by single-token
-//     waves of 16-byte lanes and with non-temporal stores otherwise, and
-//     residency is capped to about 24 KiB of loads in flight per CU (12
-//     waves of 2 KiB rows; see copy_waves_per_cu): the rows land at
-//     scattered slots, and fewer concurrent write streams measured faster;
+//   * copy: cache rows are written with non-temporal stores (which leave no
+//     written lines behind for the next kernel), and residency is capped to
+//     about 24 KiB of loads in flight per CU (12 waves of 2 KiB rows; see
+//     copy_waves_per_cu): the rows land at scattered slots, and fewer
+//     concurrent write streams measured faster;
 //   * fp8: the quantised rows are written with the sc1 cache policy through a
 //     per-row buffer descriptor, at full occupancy (the conversion needs the
 //     latency hiding);
@@ -250,22 +250,14 @@ __global__ __launch_bounds__(kCopyBlockThreads) void kvstore_copy_kernel(const C
       continue;
     }
     uint8_t* dst = cache + loc[t] * p.cache_stride;
-    if constexpr (VW == 16 && kTok == 1) {
-      // sc1 buffer stores: the 2 KiB-row prefill copy 48.0 against 48.6 us
-      // with non-temporal ones (same residency cap); waves of 8 tokens keep
-      // non-temporal stores (the wide strided copy 7.8 against 8.1 us).
-      const __amdgpu_buffer_rsrc_t rs = row_rsrc(dst);
+    // Non-temporal stores: sc1 stores timed 48.0 against 48.6 us for the
+    // prefill copy alone, but left written lines for the next kernel to
+    // write back (copy then fused FP8 store, alternating: 68.4 against 66.1
+    // us per pair).
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        const uint32_t col = col0 + c * kChunk;
-        if (col < p.row_bytes) __builtin_amdgcn_raw_buffer_store_b128(r[t][c], rs, (int)col, 0, 16);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        const uint32_t col = col0 + c * kChunk;
-        if (col < p.row_bytes) storev<VW>(dst, col, r[t][c]);
-      }
+    for (int c = 0; c < kChunks; ++c) {
+      const uint32_t col = col0 + c * kChunk;
+      if (col < p.row_bytes) storev<VW>(dst, col, r[t][c]);
     }
   }
 }
