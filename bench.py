@@ -985,7 +985,19 @@ def cpu_baseline(c3, c4, reps):
                       f"16384 tok, set 0) into full-size host caches, {sum(times):.1f} s of "
                       f"CPU work; median run",
             "seconds_per_step": round(t, 4),
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "host_cpu_model": host_cpu_model()}
+
+
+def host_cpu_model():
+    """The host CPU's model name from /proc/cpuinfo, or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 if __name__ == "__main__":

@@ -81,6 +81,7 @@ def test_bench_line_contract():
     assert rf["frac_of_serial_bound"] is None and rf["frac_of_destination_bound"] is None
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] >= 1 and cb["value"] > 0 and cb["sample"]
+    assert "host_cpu_model" in cb and cb["host_cpus"] >= 1
 
 
 def test_plain_reference_library_exports():
