@@ -88,3 +88,18 @@ def test_fp8_stores_match_format_and_cache_dtype():
     for c in (u8, e4):
         with pytest.raises(ValueError, match="GPU"):
             kv.store_kv_fp8_paged_dynamic(k3, k3, c, c, idx, sc, sc, page_size=16)
+
+
+def test_import_without_the_library_raises(tmp_path):
+    """The package has no CPU or torch fallback: a copy of it without
+    libkvstore.so refuses to import."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = tmp_path / "fp8_kv_quantization_amd"
+    pkg.mkdir()
+    shutil.copy(kv.__file__, pkg / "__init__.py")
+    r = subprocess.run([sys.executable, "-c", "import fp8_kv_quantization_amd"], cwd=tmp_path,
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode != 0
+    assert "ImportError" in r.stderr and "libkvstore.so is not built" in r.stderr
