@@ -53,9 +53,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kWave = 64;                     // lanes per wavefront (CDNA)
 constexpr int kWavesPerBlock = 2;             // fp8 kernels
 constexpr int kBlockThreads = kWave * kWavesPerBlock;
-// fp8 kernel with dynamic scales: per token, the block's waves store their
-// scales with one instruction (4 waves: 17.97 us against 18.08 for 2 and
-// 18.15 for 8 on the 16384-token workload)
+// fp8 kernel with dynamic scales: the block's waves store their scales with
+// one instruction (per token, 4 waves: 17.97 us against 18.08 for 2 and 18.15
+// for 8 on the 16384-token workload)
 constexpr int kDynWavesPerBlock = 4;
 constexpr int kCopyWavesPerBlock = 2;         // copy kernel
 constexpr int kCopyBlockThreads = kWave * kCopyWavesPerBlock;
@@ -632,6 +632,7 @@ __global__ __launch_bounds__(kBlockThreads) void kvstore_fp8_paged_kernel(const 
 // Fused e4m3fn quantise + paged store with dynamic scales.
 // ---------------------------------------------------------------------------
 constexpr int kMaxDynPasses = 4;   // whole row in one wave: up to 4096 elements
+constexpr int kMaxDynHeads = kMaxDynPasses * 1024 / 16;  // heads of at least 16 elements
 
 struct Fp8DynParams {
   Fp8Params base;                  // inv_k / inv_v unused
@@ -736,10 +737,9 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
   const uint32_t lane = threadIdx.x % kWave;
   const uint32_t w = threadIdx.x / kWave;
   const uint32_t i = wave_uniform(blockIdx.x * kDynWavesPerBlock + w);
-  // Per token, the waves of a block meet at a barrier before the scale store,
-  // so a wave past the batch works on the last token and stores nothing.
+  // The waves of a block meet at a barrier before the scale store, so a wave
+  // past the batch works on the last token and stores nothing.
   const bool valid = i < p.batch;
-  if (kPerHead && !valid) return;
   const uint32_t token = p.token_base + (valid ? i : p.batch - 1);
   const bool is_v = blockIdx.y != 0;
 
@@ -859,20 +859,28 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
     sb[j] = dyn_scale(mag_to_float<kFp16>(mb[j]));
   }
 
-  // Per token, the scales of the block's waves (consecutive tokens) go
-  // through LDS to wave 0, which stores them with one instruction after the
-  // rows: where the tokens sit in consecutive slots the scales leave as one
-  // memory request instead of one per wave (16384-token FP8 workload: 17.97
-  // us with blocks of four waves, 18.08 with two, 18.15 with eight, 18.6-18.7
-  // with a store per wave; the barrier after the row stores rather than
-  // before them 17.84 against 17.99; per-head scales measured no gain).
-  // Every wave of the block reaches the barrier.
-  __shared__ float s_val[kDynWavesPerBlock];
+  // The scales of the block's waves (consecutive tokens) go through LDS to
+  // wave 0, which stores them after the rows, behind a barrier that every
+  // wave of the block reaches: where the tokens sit in consecutive slots the
+  // scales leave as one memory request (per token-head, up to 64 of them per
+  // instruction) instead of one or two per wave.  16384-token FP8 workload:
+  // per token 17.97 us with blocks of four waves, 18.08 with two, 18.15 with
+  // eight, 18.6-18.7 with a store per wave, and 17.84 against 17.99 with the
+  // barrier after the row stores rather than before them; per token-head
+  // 18.35-18.46 against 18.66-18.93 with two stores per wave.
+  __shared__ float s_val[kDynWavesPerBlock][kPerHead ? kMaxDynHeads : 1];
   __shared__ float* s_at[kDynWavesPerBlock];
+  if (lane == 0) s_at[w] = valid && in_range ? reinterpret_cast<float*>(scales) : nullptr;
   if constexpr (!kPerHead) {
-    if (lane == 0) {
-      s_val[w] = sa[0];
-      s_at[w] = valid && in_range ? reinterpret_cast<float*>(scales) : nullptr;
+    if (lane == 0) s_val[w][0] = sa[0];
+  } else if ((lane & (gph - 1)) == 0) {
+    // the first lane of each head's gph lanes, for the head of each of its
+    // two groups (for gph = 128, lane 0: both groups lie in the pass's head)
+#pragma unroll
+    for (int j = 0; j < kPasses; ++j) {
+      const uint32_t g = j * (2u * kWave) + lane;
+      if (g < groups) s_val[w][g >> gsh] = sa[j];
+      if (g + kWave < groups) s_val[w][(g + kWave) >> gsh] = sb[j];
     }
   }
   if (valid && !in_range && lane == 0 && !is_v) report_bad_token(token);
@@ -887,28 +895,23 @@ __global__ __launch_bounds__(kWave * kDynWavesPerBlock) void kvstore_fp8_dynamic
       const u32x4 q = quantize16_checked<kFp16, false>(a[j], b[j], ia, ib);
       store8_sc1(dst, da[j], u32x2{q.x, q.y});
       if (has_b) store8_sc1(dst, db[j], u32x2{q.z, q.w});
-      // Per head, one lane per group writes its scale: the first of each
-      // head's gph lanes (for gph = 128, lane 0 of the pass), for the head of
-      // each of its two groups; non-temporal (18.55-18.61 against 18.68-18.97
-      // us with default-policy stores on the 16384-token workload).
-      if constexpr (kPerHead) {
-        if (gph > kWave) {
-          if (lane == 0)
-            __builtin_nontemporal_store(sa[j],
-                                        reinterpret_cast<float*>(scales + (g >> gsh) * s_head));
-        } else if ((lane & (gph - 1)) == 0) {
-          __builtin_nontemporal_store(sa[j], reinterpret_cast<float*>(scales + (g >> gsh) * s_head));
-          if (has_b)
-            __builtin_nontemporal_store(
-                sb[j], reinterpret_cast<float*>(scales + ((g + kWave) >> gsh) * s_head));
-        }
-      }
     }
   }
+  __syncthreads();
+  if (w != 0) return;
   if constexpr (!kPerHead) {
-    __syncthreads();
-    if (w == 0 && lane < (uint32_t)kDynWavesPerBlock && s_at[lane] != nullptr)
-      *s_at[lane] = s_val[lane];
+    if (lane < (uint32_t)kDynWavesPerBlock && s_at[lane] != nullptr) *s_at[lane] = s_val[lane][0];
+  } else {
+    // lane e takes head e % heads of wave e / heads; per-head scale stores are
+    // non-temporal (18.55-18.61 against 18.68-18.97 us with default-policy
+    // stores, one store per head group)
+    const uint32_t heads = groups >> gsh;
+    for (uint32_t e = lane; e < (uint32_t)kDynWavesPerBlock * heads; e += kWave) {
+      const uint32_t wv = e / heads, h = e - wv * heads;
+      uint8_t* const at = reinterpret_cast<uint8_t*>(s_at[wv]);
+      if (at != nullptr)
+        __builtin_nontemporal_store(s_val[wv][h], reinterpret_cast<float*>(at + h * s_head));
+    }
   }
 }
 
