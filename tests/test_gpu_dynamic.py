@@ -95,12 +95,14 @@ def test_dynamic_full_size(per_head):
                                              (8, 64, (False, True)), (16, 128, (False, True)),
                                              (32, 128, (False, True)), (2, 576, (False,)),
                                              (4, 1024, (False, True)), (2, 32, (True,)),
-                                             (4, 256, (False, True)), (8, 512, (False, True))])
+                                             (4, 256, (False, True)), (8, 512, (False, True)),
+                                             (256, 16, (False, True)), (128, 32, (True,))])
 @pytest.mark.parametrize("src", ["bf16", "fp16"])
 def test_dynamic_head_shapes(heads, dim, modes, src):
     # Rows of one to four passes, some ending inside a pass (2 x 576), in
     # both source formats (fp16 rows of several passes load every group,
-    # clamped to the row, and zero those past it).
+    # clamped to the row, and zero those past it); 256 heads of 16 is the
+    # most head scales a row can have (every lane group a head).
     rng = np.random.Generator(np.random.PCG64(heads * 7 + dim))
     T, P, pages = 150, 16, 12
     x = rng.standard_normal((2, T, heads * dim), dtype=np.float32)
