@@ -257,6 +257,7 @@ def main():
     if not args.no_next:
         next_rows = bench_next_rows(kv, torch, c4, k4, v4, i4, S, sh)
         next_rows.update(bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh))
+        next_rows.update(bench_narrow_rows(kv, torch, c3, k3, v3, i3, S, sh))
 
     wide = bench_wide_strided(kv, torch, dev, kvgen, to_dev)
     traffic = stored_traffic()
@@ -778,6 +779,46 @@ def bench_small_rows(kv, torch, c3, k3, v3, i3, S, sh, n=100):
         "plain_copy_same_bytes_us": None if plain is None else round(plain, 3),
         "plain_copy_kib_per_wave": plain_kib,
         "frac_of_plain_copy": None if plain is None else round(plain / us, 4)}}
+
+
+def bench_narrow_rows(kv, torch, c3, k3, v3, i3, S, sh, n=50):
+    """Rows whose size is a multiple of 8 or 4 bytes but not of 16, which the
+    copy moves with 8- or 4-byte lanes: the prefill copy's tokens and index
+    sets, each row the first bytes of the token's 2 KiB row (input stride
+    2 KiB), cache rows at a stride of their own size; beside each, the
+    16-byte-lane row of the next multiple of 64 bytes in the same run."""
+    dev = k3[0].device
+    T = c3.num_tokens
+    out = {}
+    for R, name in ((1024, "copy_1024B_rows_16B_lanes"), (1000, "copy_1000B_rows_8B_lanes"),
+                    (512, "copy_512B_rows_16B_lanes"), (500, "copy_500B_rows_4B_lanes")):
+        kc = torch.full((c3.slots, R), 0xFF, dtype=torch.uint8, device=dev)
+        vc = torch.full_like(kc, 0xFF)
+
+        def call(s, kc=kc, vc=vc, R=R):
+            st = kv.kvstore_copy(k3[s].data_ptr(), v3[s].data_ptr(), kc.data_ptr(), vc.data_ptr(),
+                                 i3[s].data_ptr(), kv.IDX_I32, 1, R, c3.in_stride_bytes,
+                                 c3.in_stride_bytes, R, T, c3.slots, sh)
+            if st:
+                raise kv.KVStoreError(st, "kvstore_copy")
+
+        us = time_calls(torch, call, S, n)
+        st, _, _ = kv.kvstore_check_error(sh)
+        assert st == kv.OK
+        # every stored row of set S - 1 (the last call) equals its input bytes
+        ii = i3[(n - 1) % S].long()[:64]
+        src = k3[(n - 1) % S].view(torch.uint8).view(T, -1)[:64, :R]
+        assert torch.equal(kc.index_select(0, ii), src), name
+        b = 2 * T * R * 2 + T * 4
+        lanes = 16 if R % 16 == 0 else 8 if R % 8 == 0 else 4
+        out[name] = {
+            "workload": f"prefill copy's tokens and slots ({T} tok, int32, 2^21 slots in "
+                        f"16-slot pages), {R} B rows, {lanes}-byte lanes",
+            "avg_launch_us": round(us, 3), "bytes": b, "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+            "frac_of_peak": round(b / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        del kc, vc
+        torch.cuda.empty_cache()
+    return {"copy_rows_off_16_bytes": out}
 
 
 def bench_decode(kv, torch, dev, kvgen, to_dev, n_workload, label):
