@@ -482,8 +482,8 @@ def _plain_lib():
     lib.bench_plain_read2_write1.argtypes = [vp, vp, i64, vp]
     lib.bench_plain_read.argtypes = [vp, vp, i64, u32, vp]
     lib.bench_plain_write.argtypes = [vp, i64, u32, vp]
-    lib.bench_plain_scatter_write.argtypes = [vp, vp, vp, i64, i64, i64, i64, u32, ctypes.c_int,
-                                              vp]
+    for name in ("bench_plain_scatter_write", "bench_plain_scatter_write_i64"):
+        getattr(lib, name).argtypes = [vp, vp, vp, i64, i64, i64, i64, u32, ctypes.c_int, vp]
     return lib
 
 
@@ -518,6 +518,23 @@ def plain_copy_us(torch, dev, nbytes, S, n=50):
     return best
 
 
+def plain_read_us(torch, dev, lib, sink, nbytes, S, n=50):
+    """Average time of the plain read-only kernel over `nbytes` (rounded up
+    to 16), rotating over S buffers of random bytes."""
+    sh = torch.cuda.current_stream().cuda_stream
+    nbytes = (nbytes + 15) // 16 * 16
+    bufs = [_random_bytes(torch, dev, nbytes, 200 + s) for s in range(S)]
+
+    def call(s):
+        if lib.bench_plain_read(bufs[s].data_ptr(), sink.data_ptr(), nbytes, 0x9E3779B9, sh):
+            raise RuntimeError("bench_plain_read failed")
+
+    us = time_calls(torch, call, S, n=n)
+    del bufs
+    torch.cuda.empty_cache()
+    return us
+
+
 def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, dest_sets=None, n=50):
     """Same-run attainable bound for the step's two kernels.  HBM serves a
     kernel's read and write streams one after the other, so a kernel that
@@ -538,17 +555,7 @@ def bench_serial_bound(torch, dev, c3, c4, copy_us, fp8_us, dest_sets=None, n=50
     sink = torch.zeros(1024, dtype=torch.uint8, device=dev)
 
     def read_us(nbytes, S):
-        nbytes = (nbytes + 15) // 16 * 16
-        bufs = [_random_bytes(torch, dev, nbytes, 200 + s) for s in range(S)]
-
-        def call(s):
-            if lib.bench_plain_read(bufs[s].data_ptr(), sink.data_ptr(), nbytes, 0x9E3779B9, sh):
-                raise RuntimeError("bench_plain_read failed")
-
-        us = time_calls(torch, call, S, n=n)
-        del bufs
-        torch.cuda.empty_cache()
-        return us
+        return plain_read_us(torch, dev, lib, sink, nbytes, S, n)
 
     def write_us(nbytes, S):
         nbytes = (nbytes + 15) // 16 * 16
@@ -989,7 +996,31 @@ def bench_wide_strided(kv, torch, dev, kvgen, to_dev, S=16, n=50):
     st, _, _ = kv.kvstore_check_error(sh)
     assert st == kv.OK
     b = c5.algorithmic_bytes()
-    del kc, vc, k, v
+    del k, v
+    torch.cuda.empty_cache()
+    # its two halves launched apart: plain read-only of its read bytes, and a
+    # write-only kernel writing its rows to the same slots (no reads), the
+    # faster of uncapped and 12 waves per CU.  At this launch size each half
+    # pays its own launch ramp, so their sum is no bound on the copy.
+    dest = None
+    lib = _plain_lib()
+    if lib is not None:
+        T = c5.num_tokens
+        sink = torch.zeros(1024, dtype=torch.uint8, device=dev)
+        tr = plain_read_us(torch, dev, lib, sink, 2 * T * R + T * 8, S, n)
+
+        def scatter(cap):
+            def w(s):
+                if lib.bench_plain_scatter_write_i64(kc.data_ptr(), vc.data_ptr(),
+                                                     idx[s].data_ptr(), T, R, R, c5.slots, s,
+                                                     cap, sh):
+                    raise RuntimeError("bench_plain_scatter_write_i64 failed")
+            return time_calls(torch, w, S, n)
+
+        tw = min(scatter(cap) for cap in (0, 12))
+        dest = {"read_only_us": round(tr, 3), "write_only_workload_destinations_us": round(tw, 3),
+                "sum_us": round(tr + tw, 3), "kernel_over_sum": round(us / (tr + tw), 4)}
+    del kc, vc
     torch.cuda.empty_cache()
     plain, plain_kib = plain_copy_us(torch, dev, b, S, n)
     return {"workload": "wide strided copy (8192 tok, 1x576 fp16, input row stride 640 elements, "
@@ -999,7 +1030,8 @@ def bench_wide_strided(kv, torch, dev, kvgen, to_dev, S=16, n=50):
             "rotation_sets": S,
             "plain_copy_same_bytes_us": None if plain is None else round(plain, 3),
             "plain_copy_kib_per_wave": plain_kib,
-            "frac_of_plain_copy": None if plain is None else round(plain / us, 4)}
+            "frac_of_plain_copy": None if plain is None else round(plain / us, 4),
+            "halves_launched_apart": dest}
 
 
 def cpu_baseline(c3, c4, reps):

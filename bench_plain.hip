@@ -29,10 +29,12 @@
 //                            16-byte sc1 buffer stores (measured faster than
 //                            non-temporal ones for streaming writes); 16-byte
 //                            word i holds a hash of i and `value`.
-//   bench_plain_scatter_write one hashed row of `row_bytes` (1, 2, 3 or 4
-//                            KiB) to slot idx[t] of k_cache and of v_cache
-//                            for each of `tokens` int32 indices: the prefill
-//                            copy's destinations with no reads at all (one
+//   bench_plain_scatter_write one hashed row of `row_bytes` (a multiple of
+//                            16, at most 4 KiB) to slot idx[t] of k_cache
+//                            and of v_cache for each of `tokens` int32
+//                            indices (bench_plain_scatter_write_i64: int64
+//                            indices): a store's destinations with no reads
+//                            at all (one
 //                            wave per row, blocks of 2 waves, K and V over
 //                            grid z, 16-byte sc1 buffer stores: the fastest
 //                            of sc1, non-temporal and default stores with 1,
@@ -145,26 +147,28 @@ __global__ __launch_bounds__(128) void plain_copy_n(const u32x4* __restrict__ s,
     if (base + c * kWave < n16) __builtin_nontemporal_store(r[c], d + base + c * kWave);
 }
 
+template <typename IdxT>
 __global__ __launch_bounds__(128) void plain_scatter_write(uint8_t* __restrict__ kc,
                                                            uint8_t* __restrict__ vc,
-                                                           const int32_t* __restrict__ idx,
-                                                           uint32_t tokens, uint32_t chunks,
+                                                           const IdxT* __restrict__ idx,
+                                                           uint32_t tokens, uint32_t row16,
                                                            uint64_t cache_stride, int64_t slots,
                                                            uint32_t seed) {
   const uint32_t t = __builtin_amdgcn_readfirstlane(blockIdx.x * 2 + threadIdx.x / kWave);
   if (t >= tokens) return;
   const uint32_t lane = threadIdx.x % kWave;
-  const int64_t loc = idx[t];
+  const int64_t loc = (int64_t)idx[t];
   if (loc < 0 || loc >= slots) return;
   const __amdgpu_buffer_rsrc_t row = rsrc((blockIdx.z ? vc : kc) + (uint64_t)loc * cache_stride);
   const uint32_t salt = seed ^ (blockIdx.z ? 0x5BD1E995u : 0u);
 #pragma unroll
   for (uint32_t c = 0; c < 4; ++c) {
-    if (c < chunks) {
-      const uint32_t h = (t * 0x9E3779B1u + c * kWave + lane) ^ salt;
+    const uint32_t w = c * kWave + lane;  // 16-byte word of the row
+    if (w < row16) {
+      const uint32_t h = (t * 0x9E3779B1u + w) ^ salt;
       __builtin_amdgcn_raw_buffer_store_b128(
-          u32x4{h, h ^ 0x85EBCA6Bu, h ^ 0xC2B2AE35u, h + 0x27D4EB2Fu}, row,
-          (int)((c * kWave + lane) * 16), 0, kSc1);
+          u32x4{h, h ^ 0x85EBCA6Bu, h ^ 0xC2B2AE35u, h + 0x27D4EB2Fu}, row, (int)(w * 16), 0,
+          kSc1);
     }
   }
 }
@@ -241,15 +245,15 @@ extern "C" int bench_plain_write(void* dst, int64_t bytes, uint32_t value, hipSt
   return hipGetLastError() == hipSuccess ? 0 : -5;
 }
 
-extern "C" int bench_plain_scatter_write(void* k_cache, void* v_cache, const void* idx,
-                                         int64_t tokens, int64_t row_bytes, int64_t cache_stride,
-                                         int64_t slots, uint32_t seed, int waves_per_cu,
-                                         hipStream_t stream) {
-  if (!k_cache || !v_cache || !idx || tokens <= 0 || tokens > 0x7FFFFFFFll ||
-      (row_bytes != 1024 && row_bytes != 2048 && row_bytes != 3072 && row_bytes != 4096) ||
-      cache_stride < row_bytes || cache_stride % 16 != 0 || slots <= 0 ||
-      !aligned16(k_cache) || !aligned16(v_cache) || ((uintptr_t)idx & 3u) != 0 ||
-      waves_per_cu < 0 || waves_per_cu == 1 || waves_per_cu > 64 || waves_per_cu % 2 != 0)
+template <typename IdxT>
+static int scatter_write(void* k_cache, void* v_cache, const void* idx, int64_t tokens,
+                  int64_t row_bytes, int64_t cache_stride, int64_t slots, uint32_t seed,
+                  int waves_per_cu, hipStream_t stream) {
+  if (!k_cache || !v_cache || !idx || tokens <= 0 || tokens > 0x7FFFFFFFll || row_bytes < 16 ||
+      row_bytes > 4096 || row_bytes % 16 != 0 || cache_stride < row_bytes ||
+      cache_stride % 16 != 0 || slots <= 0 || !aligned16(k_cache) || !aligned16(v_cache) ||
+      ((uintptr_t)idx % sizeof(IdxT)) != 0 || waves_per_cu < 0 || waves_per_cu == 1 ||
+      waves_per_cu > 64 || waves_per_cu % 2 != 0)
     return -1;
   uint32_t lds = 0;
   if (waves_per_cu > 0) {
@@ -263,9 +267,25 @@ extern "C" int bench_plain_scatter_write(void* k_cache, void* v_cache, const voi
     lds = (uint32_t)(per_cu / (waves_per_cu / 2) / 1280 * 1280);
   }
   const uint32_t blocks = (uint32_t)((tokens + 1) / 2);
-  hipLaunchKernelGGL(plain_scatter_write, dim3(blocks, 1, 2), dim3(128), lds, stream,
+  hipLaunchKernelGGL(plain_scatter_write<IdxT>, dim3(blocks, 1, 2), dim3(128), lds, stream,
                      static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
-                     static_cast<const int32_t*>(idx), (uint32_t)tokens,
-                     (uint32_t)(row_bytes / 1024), (uint64_t)cache_stride, slots, seed);
+                     static_cast<const IdxT*>(idx), (uint32_t)tokens, (uint32_t)(row_bytes / 16),
+                     (uint64_t)cache_stride, slots, seed);
   return hipGetLastError() == hipSuccess ? 0 : -5;
+}
+
+extern "C" int bench_plain_scatter_write(void* k_cache, void* v_cache, const void* idx,
+                                         int64_t tokens, int64_t row_bytes, int64_t cache_stride,
+                                         int64_t slots, uint32_t seed, int waves_per_cu,
+                                         hipStream_t stream) {
+  return scatter_write<int32_t>(k_cache, v_cache, idx, tokens, row_bytes, cache_stride, slots,
+                                seed, waves_per_cu, stream);
+}
+
+extern "C" int bench_plain_scatter_write_i64(void* k_cache, void* v_cache, const void* idx,
+                                             int64_t tokens, int64_t row_bytes,
+                                             int64_t cache_stride, int64_t slots, uint32_t seed,
+                                             int waves_per_cu, hipStream_t stream) {
+  return scatter_write<int64_t>(k_cache, v_cache, idx, tokens, row_bytes, cache_stride, slots,
+                                seed, waves_per_cu, stream);
 }

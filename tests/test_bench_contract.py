@@ -91,7 +91,8 @@ def test_plain_reference_library_exports():
         pytest.skip("bench_plain.so not built")
     lib = ctypes.CDLL(path)
     for name in ("bench_plain_copy", "bench_plain_copy_chunks", "bench_plain_read2_write1",
-                 "bench_plain_read", "bench_plain_write", "bench_plain_scatter_write"):
+                 "bench_plain_read", "bench_plain_write", "bench_plain_scatter_write",
+                 "bench_plain_scatter_write_i64"):
         assert hasattr(lib, name), name
     vp, i64, u32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_uint32
     lib.bench_plain_copy.argtypes = [vp, vp, i64, vp]
@@ -116,18 +117,20 @@ def test_plain_reference_library_exports():
     assert lib.bench_plain_write(None, 16, 0, None) == -1
     assert lib.bench_plain_write(16, 0, 0, None) == -1
     assert lib.bench_plain_write(24, 16, 0, None) == -1
-    lib.bench_plain_scatter_write.argtypes = [vp, vp, vp, i64, i64, i64, i64, u32, ctypes.c_int,
-                                              vp]
-    sw = lib.bench_plain_scatter_write
-    assert sw(None, 32, 64, 1, 2048, 2048, 8, 0, 0, None) == -1      # null cache
-    assert sw(16, 32, 64, 0, 2048, 2048, 8, 0, 0, None) == -1        # no tokens
-    assert sw(16, 32, 64, 1, 1536, 2048, 8, 0, 0, None) == -1        # row not 1-4 KiB in KiB
-    assert sw(16, 32, 64, 1, 2048, 1024, 8, 0, 0, None) == -1        # stride below the row
-    assert sw(16, 32, 64, 1, 2048, 2056, 8, 0, 0, None) == -1        # stride not 16-byte
-    assert sw(16, 32, 66, 1, 2048, 2048, 8, 0, 0, None) == -1        # misaligned indices
-    assert sw(16, 32, 64, 1, 2048, 2048, 0, 0, 0, None) == -1        # no slots
-    for cap in (-2, 1, 3, 66):
-        assert sw(16, 32, 64, 1, 2048, 2048, 8, 0, cap, None) == -1  # residency cap
+    for name in ("bench_plain_scatter_write", "bench_plain_scatter_write_i64"):
+        sw = getattr(lib, name)
+        sw.argtypes = [vp, vp, vp, i64, i64, i64, i64, u32, ctypes.c_int, vp]
+        assert sw(None, 32, 64, 1, 2048, 2048, 8, 0, 0, None) == -1      # null cache
+        assert sw(16, 32, 64, 0, 2048, 2048, 8, 0, 0, None) == -1        # no tokens
+        for row in (0, 8, 1000, 4112):
+            assert sw(16, 32, 64, 1, row, 4112, 8, 0, 0, None) == -1     # row not 16..4096 by 16
+        assert sw(16, 32, 64, 1, 2048, 1024, 8, 0, 0, None) == -1        # stride below the row
+        assert sw(16, 32, 64, 1, 2048, 2056, 8, 0, 0, None) == -1        # stride not 16-byte
+        assert sw(16, 32, 66, 1, 2048, 2048, 8, 0, 0, None) == -1        # misaligned indices
+        assert sw(16, 32, 64, 1, 2048, 2048, 0, 0, 0, None) == -1        # no slots
+        for cap in (-2, 1, 3, 66):
+            assert sw(16, 32, 64, 1, 2048, 2048, 8, 0, cap, None) == -1  # residency cap
+    assert lib.bench_plain_scatter_write_i64(16, 32, 68, 1, 2048, 2048, 8, 0, 0, None) == -1
 
 
 @pytest.mark.gpu
@@ -175,17 +178,23 @@ def test_plain_reference_kernels_move_the_right_bytes():
         assert lib.bench_plain_read(dst.data_ptr(), sink.data_ptr(), nbytes, 0x9E3779B9, sh) == 0
         torch.cuda.synchronize()
         assert int(sink.sum()) == 0
-    lib.bench_plain_scatter_write.argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int64,
-                                              ctypes.c_uint32, ctypes.c_int, vp]
-    for T, row, cap in ((1, 1024, 0), (37, 2048, 12), (500, 3072, 0), (64, 4096, 12)):
-        print(f"[gpu-case] plain scatter write {T} rows of {row} B, cap {cap}", flush=True)
+    for name in ("bench_plain_scatter_write", "bench_plain_scatter_write_i64"):
+        getattr(lib, name).argtypes = [vp, vp, vp, i64, i64, i64, ctypes.c_int64,
+                                       ctypes.c_uint32, ctypes.c_int, vp]
+    for T, row, cap, i64_idx in ((1, 1024, 0, False), (37, 2048, 12, False),
+                                 (500, 3072, 0, False), (64, 4096, 12, False),
+                                 (300, 1152, 0, True), (45, 16, 12, True), (70, 1008, 0, False)):
+        print(f"[gpu-case] plain scatter write {T} rows of {row} B, cap {cap}, "
+              f"int{64 if i64_idx else 32} indices", flush=True)
         slots, stride = 700, row + 64
-        idx = torch.from_numpy(np.random.default_rng(T).permutation(slots)[:T].astype(np.int32))
+        perm = np.random.default_rng(T).permutation(slots)[:T]
+        idx = torch.from_numpy(perm.astype(np.int64 if i64_idx else np.int32))
         idx[0] = slots                               # out of range: skipped
         kc = torch.zeros(slots * stride, dtype=torch.uint8, device=dev)
         vc = torch.zeros_like(kc)
-        assert lib.bench_plain_scatter_write(kc.data_ptr(), vc.data_ptr(), idx.to(dev).data_ptr(),
-                                             T, row, stride, slots, 7, cap, sh) == 0
+        fn = lib.bench_plain_scatter_write_i64 if i64_idx else lib.bench_plain_scatter_write
+        assert fn(kc.data_ptr(), vc.data_ptr(), idx.to(dev).data_ptr(), T, row, stride, slots, 7,
+                  cap, sh) == 0
         torch.cuda.synchronize()
         for cache, salt in ((kc, 7), (vc, 7 ^ 0x5BD1E995)):
             got = cache.view(slots, stride).cpu().numpy()
